@@ -1,0 +1,345 @@
+/*
+ * oracle.c -- plain, slow, scalar fp64 CPU reference for block-sparse
+ * attention decoding.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link
+ * or call this file: it is used by the test-suite, by the smoke check and by
+ * the CPU-baseline leg of the benchmark, and by nothing else.  It shares no
+ * code, header, table or helper with the GPU library.
+ *
+ * Every function works on ONE sequence and ONE KV head at a time, on plain
+ * contiguous arrays:
+ *     K[t*d + i], V[t*d + i]   token t, channel i   (float; the values are the
+ *                              exact stored values, e.g. bf16 widened)
+ *     q[h*d + i]               query head h of the GQA group, channel i
+ * All arithmetic is in double.  Nothing is blocked, fused or reordered beyond
+ * what the definitions below state; everything is recomputed from scratch.
+ *
+ * Sources (page title, then section):
+ *  [ReSA]   "Rectified Sparse Attention for Efficient Long-Sequence
+ *           Generation" (research.elamur.ai summary page), sections "Summary"
+ *           and "Key points".
+ *  [SeerR]  "SeerAttention-R: Sparse Attention Adaptation for Long Reasoning"
+ *           (mlsanity.com page), section "Abstract (arXiv)".
+ *  [SAS]    "Simple Attention Sparsification" (hyper.ai page), section
+ *           "Method" (the o_SAS equation and the Top-K discretisation).
+ *  [FD]     Flash-Decoding, cited in the [ReSA] page's reference list.
+ *
+ * Readings the pages leave open are marked READING and are listed, with the
+ * reason for each, in the design notes of the repository.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_API __attribute__((visibility("default")))
+
+static int64_t orc_nblocks(int64_t T, int b) { return (T + b - 1) / b; }
+
+/* ------------------------------------------------------------------------ */
+/* 1. Block descriptors                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* [ReSA] "Summary": each memory block is described Quest-style by the
+ * channel-wise minimum and maximum of its keys.  READING: a block covers
+ * tokens [j*b, min((j+1)*b, T)); a partial last block uses only the tokens
+ * present.  mn, mx: [NB][d]. */
+ORC_API void orc_desc_minmax(const float* K, int64_t T, int d, int b,
+                             double* mn, double* mx) {
+    int64_t NB = orc_nblocks(T, b);
+    for (int64_t j = 0; j < NB; ++j) {
+        int64_t t0 = j * b;
+        int64_t t1 = (j + 1) * (int64_t)b;
+        if (t1 > T) t1 = T;
+        for (int i = 0; i < d; ++i) {
+            double lo = K[t0 * d + i];
+            double hi = lo;
+            for (int64_t t = t0 + 1; t < t1; ++t) {
+                double v = K[t * d + i];
+                if (v < lo) lo = v;
+                if (v > hi) hi = v;
+            }
+            mn[j * d + i] = lo;
+            mx[j * d + i] = hi;
+        }
+    }
+}
+
+/* [SeerR] "Abstract (arXiv)": the plug-in gate scores blocks from pooled
+ * keys, without pooling the query.  READING: the pooled key of a block is the
+ * mean of its keys.  mean: [NB][d]. */
+ORC_API void orc_desc_mean(const float* K, int64_t T, int d, int b,
+                           double* mean) {
+    int64_t NB = orc_nblocks(T, b);
+    for (int64_t j = 0; j < NB; ++j) {
+        int64_t t0 = j * b;
+        int64_t t1 = (j + 1) * (int64_t)b;
+        if (t1 > T) t1 = T;
+        for (int i = 0; i < d; ++i) {
+            double s = 0.0;
+            for (int64_t t = t0; t < t1; ++t) s += K[t * d + i];
+            mean[j * d + i] = s / (double)(t1 - t0);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* 2. Group block scores                                                     */
+/* ------------------------------------------------------------------------ */
+
+/* [ReSA] "Summary": min/max descriptors score the blocks, and one block
+ * selection is shared by all query heads of a GQA group.  READING: the score
+ * of block j for head h is sum_i max(q_hi*mn_ji, q_hi*mx_ji) -- the largest
+ * value q_h.k can take for any k inside the block's channel-wise box -- and
+ * the group score is the sum over the G heads of the group.  s: [nblk]. */
+ORC_API void orc_score_quest(const float* q, int G, int d, const double* mn,
+                             const double* mx, int64_t nblk, double* s) {
+    for (int64_t j = 0; j < nblk; ++j) {
+        double acc = 0.0;
+        for (int h = 0; h < G; ++h) {
+            for (int i = 0; i < d; ++i) {
+                double a = (double)q[h * d + i] * mn[j * d + i];
+                double c = (double)q[h * d + i] * mx[j * d + i];
+                acc += (a > c) ? a : c;
+            }
+        }
+        s[j] = acc;
+    }
+}
+
+/* [SeerR] "Abstract (arXiv)": a lightweight linear plug-in gate over pooled
+ * keys; [SAS] "Method": s = R_theta(q, {K_B}).  READING: one linear map
+ * W [d][d] (row r = output channel r) applied to the sum of the group's query
+ * heads, dotted with the block's mean key:
+ *     u = sum_h q_h;  w = W u;  s_j = w . mean_j.   s: [nblk]. */
+ORC_API void orc_score_gate(const float* q, int G, int d, const float* W,
+                            const double* mean, int64_t nblk, double* s) {
+    double* u = (double*)malloc(sizeof(double) * (size_t)d);
+    double* w = (double*)malloc(sizeof(double) * (size_t)d);
+    for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int h = 0; h < G; ++h) acc += q[h * d + i];
+        u[i] = acc;
+    }
+    for (int r = 0; r < d; ++r) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += (double)W[r * d + i] * u[i];
+        w[r] = acc;
+    }
+    for (int64_t j = 0; j < nblk; ++j) {
+        double acc = 0.0;
+        for (int r = 0; r < d; ++r) acc += w[r] * mean[j * d + r];
+        s[j] = acc;
+    }
+    free(u);
+    free(w);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 3. How many blocks to keep                                                */
+/* ------------------------------------------------------------------------ */
+
+/* [ReSA] "Key points": a dynamic top-n that always keeps the recent local
+ * blocks and never keeps fewer than a minimum count; the kept set is sized by
+ * the sparsity p (ablated at 0.9/0.95/0.98).  [SeerR] "Abstract (arXiv)":
+ * the kept set may instead be given as a token budget (4K tokens).
+ * READING: p is the fraction SKIPPED, given in basis points so that no
+ * floating point enters the count; local blocks count towards n:
+ *     n_req = budget / b                     (budget_tokens > 0)
+ *           = ceil((10000 - bp) * NB / 10000) (otherwise)
+ *     n     = min(NB, max(n_req, n_min, min(n_local, NB))). */
+ORC_API int64_t orc_block_count(int64_t NB, int b, int64_t budget_tokens,
+                                int sparsity_bp, int n_local, int n_min) {
+    int64_t n_req;
+    if (budget_tokens > 0)
+        n_req = budget_tokens / b;
+    else
+        n_req = ((int64_t)(10000 - sparsity_bp) * NB + 9999) / 10000;
+    int64_t nl = (n_local < NB) ? n_local : NB;
+    int64_t n = n_req;
+    if (n_min > n) n = n_min;
+    if (nl > n) n = nl;
+    if (n > NB) n = NB;
+    return n;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 4. Top-n selection                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* [ReSA] "Key points" (recent local blocks always kept); [SAS] "Method"
+ * (the current block is always retained; at inference the ranking is cut to
+ * discrete Top-K block indices).  The last min(n_local, NB) blocks are kept;
+ * the other n - n_local' are taken from the candidates 0..NB-n_local'-1 by
+ * repeated arg-max under the order (score descending, index ascending).
+ * READING: ties go to the lower index; the result is emitted ascending and
+ * padded with -1 up to idx_cap.  Returns the number of kept blocks. */
+ORC_API int64_t orc_select(const double* s, int64_t NB, int64_t n,
+                           int n_local, int32_t* idx, int64_t idx_cap) {
+    int64_t nl = (n_local < NB) ? n_local : NB;
+    int64_t nc = NB - nl;
+    unsigned char* keep = (unsigned char*)calloc((size_t)(NB > 0 ? NB : 1), 1);
+    for (int64_t j = nc; j < NB; ++j) keep[j] = 1;
+    for (int64_t pick = 0; pick < n - nl; ++pick) {
+        int64_t best = -1;
+        for (int64_t j = 0; j < nc; ++j) {
+            if (keep[j]) continue;
+            if (best < 0 || s[j] > s[best]) best = j; /* '>' keeps lower index on ties */
+        }
+        if (best < 0) break;
+        keep[best] = 1;
+    }
+    int64_t c = 0;
+    for (int64_t j = 0; j < NB; ++j)
+        if (keep[j]) idx[c++] = (int32_t)j;
+    for (int64_t k = c; k < idx_cap; ++k) idx[k] = -1;
+    free(keep);
+    return c;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 5. Exact softmax attention over the kept blocks                           */
+/* ------------------------------------------------------------------------ */
+
+/* [ReSA] "Summary" (attention over the selected blocks only); [SAS]
+ * "Method" (non-selected blocks are masked out of an exact softmax).  For a
+ * single query head q [d]: the attended tokens are the union of
+ * [j*b, min((j+1)*b, T)) over the kept blocks j; two passes:
+ *     z_t = scale * q.K_t,  m = max z,  l = sum exp(z_t - m),
+ *     o = sum exp(z_t - m) V_t / l,  lse = m + ln l   (natural log).
+ * o: [d]. */
+ORC_API void orc_attend(const float* q, const float* K, const float* V,
+                        int64_t T, int d, int b, const int32_t* idx,
+                        int64_t nidx, double scale, double* o, double* lse) {
+    double m = -INFINITY;
+    for (int64_t k = 0; k < nidx; ++k) {
+        int64_t t0 = (int64_t)idx[k] * b;
+        int64_t t1 = t0 + b;
+        if (t1 > T) t1 = T;
+        for (int64_t t = t0; t < t1; ++t) {
+            double z = 0.0;
+            for (int i = 0; i < d; ++i) z += (double)q[i] * K[t * d + i];
+            z *= scale;
+            if (z > m) m = z;
+        }
+    }
+    double l = 0.0;
+    for (int i = 0; i < d; ++i) o[i] = 0.0;
+    for (int64_t k = 0; k < nidx; ++k) {
+        int64_t t0 = (int64_t)idx[k] * b;
+        int64_t t1 = t0 + b;
+        if (t1 > T) t1 = T;
+        for (int64_t t = t0; t < t1; ++t) {
+            double z = 0.0;
+            for (int i = 0; i < d; ++i) z += (double)q[i] * K[t * d + i];
+            z *= scale;
+            double p = exp(z - m);
+            l += p;
+            for (int i = 0; i < d; ++i) o[i] += p * V[t * d + i];
+        }
+    }
+    for (int i = 0; i < d; ++i) o[i] /= l;
+    *lse = m + log(l);
+}
+
+/* Dense softmax attention of one query head over tokens [0, n_tok): the
+ * textbook definition, written separately from orc_attend so that the two
+ * can be checked against each other. */
+ORC_API void orc_dense_attend(const float* q, const float* K, const float* V,
+                              int64_t n_tok, int d, double scale, double* o,
+                              double* lse) {
+    double* z = (double*)malloc(sizeof(double) * (size_t)(n_tok > 0 ? n_tok : 1));
+    double m = -INFINITY;
+    for (int64_t t = 0; t < n_tok; ++t) {
+        double acc = 0.0;
+        for (int i = 0; i < d; ++i) acc += (double)q[i] * K[t * d + i];
+        z[t] = scale * acc;
+        if (z[t] > m) m = z[t];
+    }
+    double l = 0.0;
+    for (int64_t t = 0; t < n_tok; ++t) l += exp(z[t] - m);
+    for (int i = 0; i < d; ++i) {
+        double acc = 0.0;
+        for (int64_t t = 0; t < n_tok; ++t) acc += exp(z[t] - m) * V[t * d + i];
+        o[i] = acc / l;
+    }
+    *lse = m + log(l);
+    free(z);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 6. Rectification                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* [ReSA] "Summary": after every f generated tokens those tokens are
+ * re-encoded in one dense parallel pass whose keys/values overwrite their
+ * cache entries (and, through them, the block descriptors, which this oracle
+ * always recomputes from scratch).  READING: the caller supplies the
+ * re-encoded k_new/v_new [f][d]; the order is overwrite, then causal dense
+ * attention of query i (position T-f+i) over tokens 0..T-f+i.
+ * K, V [T][d] are modified in place.  q: [G][f][d]; o: [G][f][d];
+ * lse: [G][f]. */
+ORC_API void orc_rectify(const float* q, int G, int f, float* K, float* V,
+                         int64_t T, int d, const float* k_new,
+                         const float* v_new, double scale, double* o,
+                         double* lse) {
+    for (int i = 0; i < f; ++i) {
+        for (int c = 0; c < d; ++c) {
+            K[(T - f + i) * d + c] = k_new[i * d + c];
+            V[(T - f + i) * d + c] = v_new[i * d + c];
+        }
+    }
+    for (int h = 0; h < G; ++h) {
+        for (int i = 0; i < f; ++i) {
+            orc_dense_attend(q + ((int64_t)h * f + i) * d, K, V, T - f + i + 1,
+                             d, scale, o + ((int64_t)h * f + i) * d,
+                             lse + (int64_t)h * f + i);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* 7. One whole sparse decode step for one (sequence, KV head) group        */
+/* ------------------------------------------------------------------------ */
+
+/* The plain definition of a decode step after the new token has been
+ * appended (the query attends to its own token): rebuild all descriptors,
+ * score the candidate blocks, count, select, attend for each of the G query
+ * heads.  desc_kind 0 = min/max (Quest), 1 = mean-pooled keys with gate W.
+ * idx: [idx_cap]; returns the kept count.  o: [G][d]; lse: [G];
+ * scores (optional, may be NULL): [NB] with the candidates' scores (the local
+ * blocks' entries are left as NaN). */
+ORC_API int64_t orc_decode_group(const float* q, int G, const float* K,
+                                 const float* V, int64_t T, int d, int b,
+                                 int desc_kind, const float* W,
+                                 int64_t budget_tokens, int sparsity_bp,
+                                 int n_local, int n_min, double scale,
+                                 int32_t* idx, int64_t idx_cap, double* o,
+                                 double* lse, double* scores) {
+    int64_t NB = orc_nblocks(T, b);
+    int64_t nl = (n_local < NB) ? n_local : NB;
+    double* s = (double*)malloc(sizeof(double) * (size_t)NB);
+    for (int64_t j = 0; j < NB; ++j) s[j] = NAN;
+    if (desc_kind == 0) {
+        double* mn = (double*)malloc(sizeof(double) * (size_t)(NB * d));
+        double* mx = (double*)malloc(sizeof(double) * (size_t)(NB * d));
+        orc_desc_minmax(K, T, d, b, mn, mx);
+        orc_score_quest(q, G, d, mn, mx, NB - nl, s);
+        free(mn);
+        free(mx);
+    } else {
+        double* mean = (double*)malloc(sizeof(double) * (size_t)(NB * d));
+        orc_desc_mean(K, T, d, b, mean);
+        orc_score_gate(q, G, d, W, mean, NB - nl, s);
+        free(mean);
+    }
+    int64_t n = orc_block_count(NB, b, budget_tokens, sparsity_bp, n_local, n_min);
+    int64_t cnt = orc_select(s, NB, n, n_local, idx, idx_cap);
+    for (int h = 0; h < G; ++h)
+        orc_attend(q + (int64_t)h * d, K, V, T, d, b, idx, cnt, scale,
+                   o + (int64_t)h * d, lse + h);
+    if (scores) memcpy(scores, s, sizeof(double) * (size_t)NB);
+    free(s);
+    return cnt;
+}
