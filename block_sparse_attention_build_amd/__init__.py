@@ -1,0 +1,230 @@
+"""Python binding of libbsa (block-sparse attention decoding on MI355X).
+
+A thin ctypes layer over the C ABI in include/bsa.h: the functions below have
+the C entry points' names and arguments, take torch tensors that live on the
+GPU, and pass their data pointers and the current HIP stream.  torch supplies
+device memory and streams only; every step of the computation runs in the
+library's HIP kernels.  There is no CPU fallback: if libbsa.so is missing or
+fails to load, every call raises.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIBPATH = os.path.join(_PKG, "libbsa.so")
+
+# status codes (bsa_status)
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_PARAM, ERR_WORKSPACE, ERR_HIP = range(7)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+DESC_MINMAX, DESC_MEANPOOL = 0, 1
+OP_SELECT, OP_DECODE, OP_RECTIFY = 1, 2, 3
+
+EXPORTS = ("bsa_build_block_desc", "bsa_select_blocks", "bsa_sparse_decode",
+           "bsa_rectify_chunk", "bsa_workspace_size", "bsa_block_count",
+           "bsa_status_string")
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class c_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "Hq", "Hkv", "d", "block", "max_blocks", "kv_dtype", "desc_kind")]
+
+
+class c_cache(ctypes.Structure):
+    _fields_ = [("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+                ("desc", ctypes.c_void_p)]
+
+
+class c_select_params(ctypes.Structure):
+    _fields_ = [("budget_tokens", ctypes.c_int32), ("sparsity_bp", ctypes.c_int32),
+                ("n_local", ctypes.c_int32), ("n_min", ctypes.c_int32),
+                ("n_max", ctypes.c_int32), ("gate_w", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libbsa.so (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIBPATH):
+        raise RuntimeError(f"libbsa.so not found at {_LIBPATH}: build it first "
+                           "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(_LIBPATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    pl, pc, pp = ctypes.POINTER(c_layout), ctypes.POINTER(c_cache), ctypes.POINTER(c_select_params)
+    L.bsa_build_block_desc.argtypes = [pl, pc, vp, vp, i32, vp, vp]
+    L.bsa_select_blocks.argtypes = [pl, pc, vp, pp, vp, vp, vp, sz, vp]
+    L.bsa_sparse_decode.argtypes = [pl, pc, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
+    L.bsa_rectify_chunk.argtypes = [pl, pc, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
+    L.bsa_workspace_size.argtypes = [pl, i32, i32]
+    L.bsa_workspace_size.restype = sz
+    L.bsa_block_count.argtypes = [pp, i32, i32]
+    L.bsa_block_count.restype = i32
+    L.bsa_status_string.argtypes = [ctypes.c_int]
+    L.bsa_status_string.restype = ctypes.c_char_p
+    for fn in (L.bsa_build_block_desc, L.bsa_select_blocks, L.bsa_sparse_decode,
+               L.bsa_rectify_chunk):
+        fn.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_string(status):
+    return lib().bsa_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status, what):
+    if status != OK:
+        raise BsaError(status, what)
+
+
+# ---------------------------------------------------------------------------
+# Shape / parameter records
+# ---------------------------------------------------------------------------
+
+@dataclass
+class Layout:
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    block: int
+    max_blocks: int
+    kv_dtype: int = DTYPE_BF16
+    desc_kind: int = DESC_MINMAX
+
+    def c(self):
+        return c_layout(self.B, self.Hq, self.Hkv, self.d, self.block, self.max_blocks,
+                        self.kv_dtype, self.desc_kind)
+
+    @property
+    def G(self):
+        return self.Hq // self.Hkv
+
+    def torch_dtype(self):
+        import torch
+        return torch.bfloat16 if self.kv_dtype == DTYPE_BF16 else torch.float32
+
+
+@dataclass
+class SelectParams:
+    budget_tokens: int = 0
+    sparsity_bp: int = 0
+    n_local: int = 1
+    n_min: int = 0
+    n_max: int = 0
+    gate_w: Optional[object] = None  # torch bf16 [d, d] on the device
+
+    def c(self):
+        return c_select_params(self.budget_tokens, self.sparsity_bp, self.n_local, self.n_min,
+                               self.n_max, None if self.gate_w is None else self.gate_w.data_ptr())
+
+
+@dataclass
+class Cache:
+    """Device tensors of one paged cache (any torch tensors of the documented
+    shapes; see PagedCache for an allocator)."""
+    k_pool: object
+    v_pool: object
+    page_table: object
+    seq_lens: object
+    desc: object
+
+    def c(self):
+        return c_cache(self.k_pool.data_ptr(), self.v_pool.data_ptr(), self.page_table.data_ptr(),
+                       self.seq_lens.data_ptr(), self.desc.data_ptr())
+
+
+def allocate_cache(layout: Layout, num_pages: Optional[int] = None, page_table=None,
+                   device="cuda"):
+    """Allocate pools, descriptors and seq_lens with torch (device memory
+    only).  page_table defaults to sequence s owning pages
+    [s*max_blocks, (s+1)*max_blocks) in order."""
+    import torch
+    L = layout
+    if num_pages is None:
+        num_pages = L.B * L.max_blocks
+    dt = L.torch_dtype()
+    page_elems = L.block * L.d
+    k_pool = torch.empty(num_pages, L.Hkv, page_elems, dtype=dt, device=device)
+    v_pool = torch.empty(num_pages, L.Hkv, page_elems, dtype=dt, device=device)
+    if page_table is None:
+        page_table = torch.arange(L.B * L.max_blocks, dtype=torch.int32,
+                                  device=device).view(L.B, L.max_blocks)
+    else:
+        page_table = page_table.to(device=device, dtype=torch.int32).contiguous()
+    if L.desc_kind == DESC_MINMAX:
+        desc = torch.empty(L.B, L.Hkv, L.max_blocks, 2, L.d, dtype=dt, device=device)
+    else:
+        desc = torch.empty(L.B, L.Hkv, L.max_blocks, L.d, dtype=torch.float32, device=device)
+    seq_lens = torch.zeros(L.B, dtype=torch.int32, device=device)
+    return Cache(k_pool, v_pool, page_table, seq_lens, desc)
+
+
+# ---------------------------------------------------------------------------
+# Entry points (same names as the C ABI, without the prefix)
+# ---------------------------------------------------------------------------
+
+def workspace_size(layout: Layout, op: int, n_max_or_f: int) -> int:
+    return int(lib().bsa_workspace_size(ctypes.byref(layout.c()), op, n_max_or_f))
+
+
+def block_count(params: SelectParams, NB: int, block: int) -> int:
+    return int(lib().bsa_block_count(ctypes.byref(params.c()), NB, block))
+
+
+def build_block_desc(layout: Layout, cache: Cache, k_new=None, v_new=None, n_new: int = 0,
+                     range_begin=None, stream=None):
+    """Append n_new tokens per sequence (k_new/v_new [B, Hkv, n_new, d]) or,
+    with k_new = v_new = None, rebuild descriptors from range_begin [B]."""
+    st = lib().bsa_build_block_desc(ctypes.byref(layout.c()), ctypes.byref(cache.c()),
+                                    _ptr(k_new), _ptr(v_new), int(n_new), _ptr(range_begin),
+                                    _stream(stream))
+    _check(st, "bsa_build_block_desc")
+
+
+def select_blocks(layout: Layout, cache: Cache, q, params: SelectParams, idx, cnt, ws,
+                  stream=None):
+    st = lib().bsa_select_blocks(ctypes.byref(layout.c()), ctypes.byref(cache.c()), _ptr(q),
+                                 ctypes.byref(params.c()), _ptr(idx), _ptr(cnt), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "bsa_select_blocks")
+
+
+def sparse_decode(layout: Layout, cache: Cache, q, idx, cnt, n_max: int, softmax_scale: float,
+                  o, lse, ws, stream=None):
+    st = lib().bsa_sparse_decode(ctypes.byref(layout.c()), ctypes.byref(cache.c()), _ptr(q),
+                                 _ptr(idx), _ptr(cnt), int(n_max), float(softmax_scale), _ptr(o),
+                                 _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream))
+    _check(st, "bsa_sparse_decode")
+
+
+def rectify_chunk(layout: Layout, cache: Cache, q, k_new, v_new, f: int, softmax_scale: float,
+                  o, lse, ws, stream=None):
+    st = lib().bsa_rectify_chunk(ctypes.byref(layout.c()), ctypes.byref(cache.c()), _ptr(q),
+                                 _ptr(k_new), _ptr(v_new), int(f), float(softmax_scale),
+                                 _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream))
+    _check(st, "bsa_rectify_chunk")

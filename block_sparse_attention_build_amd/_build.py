@@ -1,0 +1,60 @@
+"""Build libbsa.so (the HIP kernels + C ABI) for gfx950 with hipcc.
+
+Every .hip file under csrc/ is compiled to an object in parallel, then linked
+into block_sparse_attention_build_amd/libbsa.so.  Objects go to _build/ at the
+repository root.
+"""
+import concurrent.futures as cf
+import glob
+import os
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libbsa.so")
+ARCH = "gfx950"
+
+CXXFLAGS = [
+    "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
+    f"--offload-arch={ARCH}",
+    # no packed fp32 (v_pk_*_f32) instructions anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _compile(src, verbose):
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = ["hipcc", *CXXFLAGS, "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # the host pass does not know the packed-fp32 feature: that warning is noise
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines()
+            if "packed-fp32-ops" not in ln]
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs), flush=True)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    tmp = LIB + ".tmp"
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

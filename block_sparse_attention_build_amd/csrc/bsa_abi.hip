@@ -1,0 +1,248 @@
+// bsa_abi.hip -- the extern "C" surface declared in include/bsa.h.
+// Every entry point validates its arguments on the host before any HIP call,
+// carves its workspace, enqueues its kernels on the caller's stream and
+// returns; nothing is allocated, nothing is synchronised.
+#include <math.h>
+#include <stddef.h>
+
+#include "../../include/bsa.h"
+#include "bsa_device.h"
+#include "bsa_internal.h"
+
+using namespace bsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bsa_status check_layout(const bsa_layout* L) {
+    if (!L) return BSA_ERR_NULL;
+    if (L->B < 1 || L->Hq < 1 || L->Hkv < 1 || L->max_blocks < 1) return BSA_ERR_SHAPE;
+    if (L->Hq % L->Hkv != 0) return BSA_ERR_SHAPE;
+    if (L->Hq / L->Hkv > 16) return BSA_ERR_UNSUPPORTED;
+    if (L->d != 64 && L->d != 128) return BSA_ERR_UNSUPPORTED;
+    if (L->block != 32 && L->block != 64 && L->block != 128 && L->block != 256)
+        return BSA_ERR_UNSUPPORTED;
+    if (L->kv_dtype != BSA_DTYPE_F32 && L->kv_dtype != BSA_DTYPE_BF16) return BSA_ERR_UNSUPPORTED;
+    if (L->desc_kind != BSA_DESC_MINMAX && L->desc_kind != BSA_DESC_MEANPOOL)
+        return BSA_ERR_UNSUPPORTED;
+    if (L->max_blocks > 32768) return BSA_ERR_UNSUPPORTED;
+    if (static_cast<int64_t>(L->max_blocks) * L->block > (1ll << 30)) return BSA_ERR_UNSUPPORTED;
+    return BSA_OK;
+}
+
+bsa_status check_cache(const bsa_cache* C) {
+    if (!C) return BSA_ERR_NULL;
+    if (!C->k_pool || !C->v_pool || !C->page_table || !C->seq_lens || !C->desc)
+        return BSA_ERR_NULL;
+    return BSA_OK;
+}
+
+CacheArgs make_args(const bsa_layout* L, const bsa_cache* C) {
+    CacheArgs a;
+    a.k_pool = C ? C->k_pool : nullptr;
+    a.v_pool = C ? C->v_pool : nullptr;
+    a.page_table = C ? C->page_table : nullptr;
+    a.seq_lens = C ? C->seq_lens : nullptr;
+    a.desc = C ? C->desc : nullptr;
+    a.B = L->B;
+    a.Hq = L->Hq;
+    a.Hkv = L->Hkv;
+    a.G = L->Hq / L->Hkv;
+    a.d = L->d;
+    a.block = L->block;
+    a.max_blocks = L->max_blocks;
+    a.dtype = L->kv_dtype == BSA_DTYPE_BF16 ? kBF16 : kF32;
+    a.desc_kind = L->desc_kind == BSA_DESC_MINMAX ? kMinMax : kMeanPool;
+    return a;
+}
+
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+struct DecodeWs {
+    size_t o_part, lse_part, total;
+    int splits;
+};
+DecodeWs decode_ws(const CacheArgs& c, int n_max) {
+    DecodeWs w;
+    w.splits = decode_splits(c, n_max);
+    const size_t rows = static_cast<size_t>(c.B) * c.Hq;
+    w.o_part = 0;
+    w.lse_part = align_up(rows * w.splits * c.d * sizeof(float));
+    w.total = w.lse_part + align_up(rows * w.splits * sizeof(float));
+    return w;
+}
+
+struct RectifyWs {
+    size_t o_part, lse_part, total;
+    int splits, chunk_tiles;
+};
+RectifyWs rectify_ws(const CacheArgs& c, int f) {
+    RectifyWs w;
+    rectify_splits(c, f, &w.splits, &w.chunk_tiles);
+    const size_t rows = static_cast<size_t>(c.B) * c.Hq * f;
+    w.o_part = 0;
+    w.lse_part = align_up(rows * w.splits * c.d * sizeof(float));
+    w.total = w.lse_part + align_up(rows * w.splits * sizeof(float));
+    return w;
+}
+
+size_t select_ws(const CacheArgs& c) {
+    return align_up(static_cast<size_t>(c.B) * c.Hkv * c.max_blocks * sizeof(float));
+}
+
+bsa_status check_select_params(const bsa_layout* L, const bsa_select_params* P) {
+    if (!P) return BSA_ERR_NULL;
+    if (P->n_local < 1 || P->n_min < 0 || P->budget_tokens < 0) return BSA_ERR_PARAM;
+    if (P->budget_tokens == 0 && (P->sparsity_bp < 0 || P->sparsity_bp >= 10000))
+        return BSA_ERR_PARAM;
+    if (L->desc_kind == BSA_DESC_MEANPOOL && !P->gate_w) return BSA_ERR_PARAM;
+    if (P->n_max < 1) return BSA_ERR_PARAM;
+    const int need = block_count(L->max_blocks, L->block, P->budget_tokens, P->sparsity_bp,
+                                 P->n_local, P->n_min);
+    if (P->n_max < need) return BSA_ERR_PARAM;
+    return BSA_OK;
+}
+
+bsa_status hip_status(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bsa_status_string(bsa_status status) {
+    switch (status) {
+        case BSA_OK: return "ok";
+        case BSA_ERR_NULL: return "a required pointer is NULL";
+        case BSA_ERR_SHAPE: return "inconsistent shape (B, Hq, Hkv, max_blocks)";
+        case BSA_ERR_UNSUPPORTED: return "unsupported dtype, head dim, block size or descriptor kind";
+        case BSA_ERR_PARAM: return "parameter out of range";
+        case BSA_ERR_WORKSPACE: return "workspace too small";
+        case BSA_ERR_HIP: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int32_t bsa_block_count(const bsa_select_params* params, int32_t NB, int32_t block) {
+    if (!params || NB < 0 || block < 1) return -1;
+    if (params->n_local < 1 || params->n_min < 0 || params->budget_tokens < 0) return -1;
+    if (params->budget_tokens == 0 && (params->sparsity_bp < 0 || params->sparsity_bp >= 10000))
+        return -1;
+    return block_count(NB, block, params->budget_tokens, params->sparsity_bp, params->n_local,
+                       params->n_min);
+}
+
+size_t bsa_workspace_size(const bsa_layout* layout, int32_t op, int32_t n_max_or_f) {
+    if (check_layout(layout) != BSA_OK || n_max_or_f < 1) return 0;
+    const CacheArgs c = make_args(layout, nullptr);
+    switch (op) {
+        case BSA_OP_SELECT: return select_ws(c);
+        case BSA_OP_DECODE: return decode_ws(c, n_max_or_f).total;
+        case BSA_OP_RECTIFY: return rectify_ws(c, n_max_or_f).total;
+        default: return 0;
+    }
+}
+
+bsa_status bsa_build_block_desc(const bsa_layout* layout, const bsa_cache* cache,
+                                const void* k_new, const void* v_new, int32_t n_new,
+                                const int32_t* range_begin, hipStream_t stream) {
+    bsa_status st = check_layout(layout);
+    if (st != BSA_OK) return st;
+    if ((st = check_cache(cache)) != BSA_OK) return st;
+    const bool append = (k_new != nullptr) || (v_new != nullptr);
+    if (append) {
+        if (!k_new || !v_new) return BSA_ERR_PARAM;
+        if (n_new < 1 || static_cast<int64_t>(n_new) >
+                             static_cast<int64_t>(layout->max_blocks) * layout->block)
+            return BSA_ERR_PARAM;
+        if (range_begin) return BSA_ERR_PARAM;
+    }
+    const CacheArgs c = make_args(layout, cache);
+    return hip_status(launch_kv_write(c, append ? kModeAppend : kModeRebuild, k_new, v_new,
+                                      append ? n_new : 0, range_begin, stream));
+}
+
+bsa_status bsa_select_blocks(const bsa_layout* layout, const bsa_cache* cache, const void* q,
+                             const bsa_select_params* params, int32_t* idx, int32_t* cnt,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+    bsa_status st = check_layout(layout);
+    if (st != BSA_OK) return st;
+    if ((st = check_cache(cache)) != BSA_OK) return st;
+    if (!q || !idx || !cnt || !ws) return BSA_ERR_NULL;
+    if ((st = check_select_params(layout, params)) != BSA_OK) return st;
+    const CacheArgs c = make_args(layout, cache);
+    if (topn_keys_per_thread(c.max_blocks) == 0) return BSA_ERR_UNSUPPORTED;
+    if (ws_bytes < select_ws(c)) return BSA_ERR_WORKSPACE;
+    SelectArgs s;
+    s.q = q;
+    s.gate_w = params->gate_w;
+    s.budget_tokens = params->budget_tokens;
+    s.sparsity_bp = params->sparsity_bp;
+    s.n_local = params->n_local;
+    s.n_min = params->n_min;
+    s.n_max = params->n_max;
+    s.idx = idx;
+    s.cnt = cnt;
+    s.scores = static_cast<float*>(ws);
+    return hip_status(launch_select(c, s, stream));
+}
+
+bsa_status bsa_sparse_decode(const bsa_layout* layout, const bsa_cache* cache, const void* q,
+                             const int32_t* idx, const int32_t* cnt, int32_t n_max,
+                             float softmax_scale, void* o, float* lse, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    bsa_status st = check_layout(layout);
+    if (st != BSA_OK) return st;
+    if ((st = check_cache(cache)) != BSA_OK) return st;
+    if (!q || !idx || !cnt || !o || !lse || !ws) return BSA_ERR_NULL;
+    if (n_max < 1 || n_max > layout->max_blocks) return BSA_ERR_PARAM;
+    if (!scale_ok(softmax_scale)) return BSA_ERR_PARAM;
+    const CacheArgs c = make_args(layout, cache);
+    const DecodeWs w = decode_ws(c, n_max);
+    if (ws_bytes < w.total) return BSA_ERR_WORKSPACE;
+    DecodeArgs a;
+    a.q = q;
+    a.idx = idx;
+    a.cnt = cnt;
+    a.n_max = n_max;
+    a.splits = w.splits;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.o_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.o_part);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.lse_part);
+    a.o = o;
+    a.lse = lse;
+    return hip_status(launch_decode(c, a, stream));
+}
+
+bsa_status bsa_rectify_chunk(const bsa_layout* layout, const bsa_cache* cache, const void* q,
+                             const void* k_new, const void* v_new, int32_t f,
+                             float softmax_scale, void* o, float* lse, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+    bsa_status st = check_layout(layout);
+    if (st != BSA_OK) return st;
+    if ((st = check_cache(cache)) != BSA_OK) return st;
+    if (!q || !k_new || !v_new || !o || !lse || !ws) return BSA_ERR_NULL;
+    if (f < 1 || static_cast<int64_t>(f) > static_cast<int64_t>(layout->max_blocks) * layout->block)
+        return BSA_ERR_PARAM;
+    if ((layout->Hq / layout->Hkv) * f > 4096) return BSA_ERR_PARAM;
+    if (!scale_ok(softmax_scale)) return BSA_ERR_PARAM;
+    const CacheArgs c = make_args(layout, cache);
+    const RectifyWs w = rectify_ws(c, f);
+    if (ws_bytes < w.total) return BSA_ERR_WORKSPACE;
+    RectifyArgs a;
+    a.q = q;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.f = f;
+    a.splits = w.splits;
+    a.chunk_tiles = w.chunk_tiles;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.o_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.o_part);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.lse_part);
+    a.o = o;
+    a.lse = lse;
+    return hip_status(launch_rectify(c, a, stream));
+}
+
+}  // extern "C"

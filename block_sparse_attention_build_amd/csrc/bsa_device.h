@@ -1,0 +1,142 @@
+// bsa_device.h -- device-side building blocks shared by the libbsa kernels:
+// storage types, bf16 conversion, the page layouts, wave reductions.
+// gfx950 (CDNA4) only: wave64, bf16 matrix-core instructions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+constexpr int kWave = 64;
+
+// dtype tags (match bsa_dtype)
+constexpr int kF32 = 0;
+constexpr int kBF16 = 1;
+// descriptor kinds (match bsa_desc_kind)
+constexpr int kMinMax = 0;
+constexpr int kMeanPool = 1;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32.  bf16 values are carried as their 16-bit patterns.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf2f(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+// Two fp32 -> packed bf16 pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+}
+
+template <int DT> struct Elem;
+template <> struct Elem<kF32> {
+    typedef float T;
+    static __device__ __forceinline__ float load(const T* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(T* p, int64_t i, float v) { p[i] = v; }
+    static __device__ __forceinline__ T from(float v) { return v; }
+};
+template <> struct Elem<kBF16> {
+    typedef uint16_t T;
+    static __device__ __forceinline__ float load(const T* p, int64_t i) { return bf2f(p[i]); }
+    static __device__ __forceinline__ void store(T* p, int64_t i, float v) { p[i] = f2bf(v); }
+    static __device__ __forceinline__ T from(float v) { return f2bf(v); }
+};
+
+// ---------------------------------------------------------------------------
+// Page layouts (element offsets inside one page of b tokens x d channels).
+// fp32: row major.  bf16: every 512 elements (1 KiB) are one 64-lane operand
+// of v_mfma_f32_16x16x32_bf16, lane L holding 8 consecutive elements at
+// L*8.  For a 16x32 (rows x k) operand the lane of (row r, k) is r + 16*(k/8)
+// and its element is k%8.
+//   K: operand A of S^T = K Q^T: rows = 16 tokens, k = 32 channels;
+//      chunk = (t/16)*(d/32) + i/32.
+//   V: operand B of O = P V: k = 32 tokens, columns = 16 channels;
+//      chunk = (t/32)*(d/16) + i/16.  Within the 32 tokens, token slot
+//      (lane group g, element e) holds token 4g+e (e < 4) or 16+4g+e-4
+//      (e >= 4): exactly the tokens the S^T accumulator of lane group g
+//      holds after two 16-token row tiles, so P needs no data movement.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int k_off_bf16(int t, int i, int d) {
+    return (((t >> 4) * (d >> 5) + (i >> 5)) << 9) + (((t & 15) + (((i & 31) >> 3) << 4)) << 3) +
+           (i & 7);
+}
+__host__ __device__ __forceinline__ int v_off_bf16(int t, int i, int d) {
+    const int u = t & 31;
+    const int g = (u & 15) >> 2;
+    const int e = (u & 3) + ((u >> 4) << 2);
+    return (((t >> 5) * (d >> 4) + (i >> 4)) << 9) + (((i & 15) + (g << 4)) << 3) + e;
+}
+template <int DT>
+__host__ __device__ __forceinline__ int k_off(int t, int i, int d) {
+    return DT == kBF16 ? k_off_bf16(t, i, d) : t * d + i;
+}
+template <int DT>
+__host__ __device__ __forceinline__ int v_off(int t, int i, int d) {
+    return DT == kBF16 ? v_off_bf16(t, i, d) : t * d + i;
+}
+
+// ---------------------------------------------------------------------------
+// Wave helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = WIDTH / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, WIDTH);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+// Order-preserving map of fp32 to uint32 (larger float -> larger key);
+// -0.0 is folded onto +0.0 first.  Inputs are not NaN.
+__device__ __forceinline__ uint32_t float_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) == 0u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Kept-block count for NB blocks ("Rectified Sparse Attention ...", Key
+// points: dynamic top-n with local blocks and a minimum count; the token
+// budget of "SeerAttention-R", Abstract).  p is the skipped fraction in basis
+// points; the local blocks count towards n.
+__host__ __device__ __forceinline__ int block_count(int NB, int block, int budget_tokens,
+                                                    int sparsity_bp, int n_local, int n_min) {
+    int n_req;
+    if (budget_tokens > 0)
+        n_req = budget_tokens / block;
+    else
+        n_req = static_cast<int>((static_cast<int64_t>(10000 - sparsity_bp) * NB + 9999) / 10000);
+    const int nl = n_local < NB ? n_local : NB;
+    int n = n_req;
+    if (n_min > n) n = n_min;
+    if (nl > n) n = nl;
+    if (n > NB) n = NB;
+    return n;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+}  // namespace bsa

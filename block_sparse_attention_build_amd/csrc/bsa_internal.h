@@ -1,0 +1,81 @@
+// bsa_internal.h -- host-side launch interface between the C ABI
+// (bsa_abi.hip) and the kernel files.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsa {
+
+struct CacheArgs {
+    void* k_pool;
+    void* v_pool;
+    const int32_t* page_table;
+    const int32_t* seq_lens;
+    void* desc;
+    int B, Hq, Hkv, G, d, block, max_blocks;
+    int dtype;      // kF32 / kBF16
+    int desc_kind;  // kMinMax / kMeanPool
+};
+
+// kv_write modes
+constexpr int kModeAppend = 0;     // write new tokens, merge into descriptors
+constexpr int kModeOverwrite = 1;  // write new tokens, rebuild touched descriptors
+constexpr int kModeRebuild = 2;    // no write, rebuild descriptors of a range
+
+hipError_t launch_kv_write(const CacheArgs& c, int mode, const void* k_new, const void* v_new,
+                           int n_new, const int32_t* range_begin, hipStream_t stream);
+
+struct SelectArgs {
+    const void* q;
+    const void* gate_w;
+    int budget_tokens, sparsity_bp, n_local, n_min, n_max;
+    int32_t* idx;
+    int32_t* cnt;
+    float* scores;  // workspace [B*Hkv][max_blocks]
+};
+hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t stream);
+// keys-per-thread bucket of the top-n kernel for a given max_blocks (0 = too many)
+int topn_keys_per_thread(int max_blocks);
+
+struct DecodeArgs {
+    const void* q;
+    const int32_t* idx;
+    const int32_t* cnt;
+    int n_max;
+    int splits;  // S: partials per (sequence, query head)
+    float scale_log2;  // softmax_scale * log2(e)
+    float* o_part;     // [B*Hq][S][d]
+    float* lse_part;   // [B*Hq][S]  (base-2 log-sum-exp of the scaled logits)
+    void* o;
+    float* lse;
+};
+hipError_t launch_decode(const CacheArgs& c, const DecodeArgs& a, hipStream_t stream);
+int decode_splits(const CacheArgs& c, int n_max);
+
+struct RectifyArgs {
+    const void* q;      // [B][Hq][f][d]
+    const void* k_new;  // [B][Hkv][f][d]
+    const void* v_new;
+    int f;
+    int splits;           // token chunks per group
+    int chunk_tiles;      // 32-token tiles per chunk
+    float scale_log2;
+    float* o_part;        // [B*Hq*f][S][d]
+    float* lse_part;      // [B*Hq*f][S]
+    void* o;
+    float* lse;
+};
+hipError_t launch_rectify(const CacheArgs& c, const RectifyArgs& a, hipStream_t stream);
+void rectify_splits(const CacheArgs& c, int f, int* splits, int* chunk_tiles);
+
+// Merge S partials of `rows` rows into o (KV dtype) and lse (natural log).
+hipError_t launch_combine(int dtype, int d, int rows, int splits, const float* o_part,
+                          const float* lse_part, void* o, float* lse, hipStream_t stream);
+// Same, but row r merges only the splits covering [0, seq_lens[r / rows_per_seq]).
+hipError_t launch_combine_ragged(int dtype, int d, int rows, int splits, const float* o_part,
+                                 const float* lse_part, void* o, float* lse,
+                                 const int32_t* seq_lens, int rows_per_seq,
+                                 int tokens_per_split, hipStream_t stream);
+
+}  // namespace bsa

@@ -1,0 +1,451 @@
+// decode.hip -- exact softmax attention over the kept blocks (split over the
+// kept tokens) and the log-sum-exp merge of the partial results.
+//
+// "Rectified Sparse Attention for Efficient Long-Sequence Generation",
+// Summary: group block-sparse attention, all query heads of a GQA group
+// reading the same kept blocks.  "Simple Attention Sparsification", Method:
+// non-selected blocks are masked out of an exact, online softmax.
+// Flash-Decoding (cited in the ReSA page's references): split the keys,
+// merge the partial (o, lse) pairs.
+//
+// bf16 path (the bandwidth-critical kernel).  One workgroup = 4 waves =
+// one (sequence, KV head, split); the split is a contiguous range of 32-token
+// tiles of the group's kept-block list, and the waves take every 4th tile.
+// Per tile a wave issues 16-byte loads of 8 KiB of K and 8 KiB of V (d=128):
+// every load instruction reads one contiguous KiB because the page layout
+// stores each KiB as one matrix-core operand.  The wave then computes
+//   S^T (32 tokens x 16 head columns) = K Q^T   with v_mfma_f32_16x16x32_bf16
+// (the group's G <= 16 heads padded to 16 columns), an online softmax per
+// head column (max across the 4 lane groups with two shuffles), and
+//   O (16 heads x d) += P V
+// where P is exactly the S^T accumulator the lane already holds (the V page
+// layout orders tokens to match), split into bf16 hi + lo parts so that the
+// weights keep ~16 mantissa bits.  K and V are read once per group, never
+// once per head.  At the end the 4 waves merge through LDS and the
+// workgroup writes one normalised partial (o, base-2 lse) per head.
+//
+// fp32 path.  Same split structure, plain VALU arithmetic (no fp32 matrix
+// operand layout is defined for the pages); used by the small fp32 cases.
+#include <math.h>
+
+#include "bsa_device.h"
+#include "bsa_internal.h"
+
+namespace bsa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+
+struct DecodeParams {
+    CacheArgs c;
+    DecodeArgs a;
+};
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Merge the per-wave (m, l, O) held in LDS and write one partial per head.
+// sm/sl: [kWaves][16]; so: [kWaves][G][D].
+__device__ __forceinline__ void merge_waves_and_store(const float* sm, const float* sl,
+                                                      const float* so, int G, int D,
+                                                      float* o_part, float* lse_part,
+                                                      int64_t head_row0, int S, int split) {
+    for (int k = threadIdx.x; k < G * D; k += kThreads) {
+        const int h = k / D;
+        const int ch = k - h * D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * 16 + h]);
+        const int64_t row = head_row0 + h;
+        float* op = o_part + (row * S + split) * D;
+        if (M == -INFINITY) {
+            op[ch] = 0.f;
+            if (ch == 0) lse_part[row * S + split] = -INFINITY;
+            continue;
+        }
+        float L = 0.f, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float sc = exp2f(sm[w * 16 + h] - M);
+            L += sl[w * 16 + h] * sc;
+            acc += so[(w * G + h) * D + ch] * sc;
+        }
+        op[ch] = acc / L;
+        if (ch == 0) lse_part[row * S + split] = M + log2f(L);
+    }
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
+    constexpr int KS = D / 32;   // k-steps of the QK product
+    constexpr int NT = D / 16;   // column tiles of the PV product
+    constexpr int TPB = BLK / 32;
+    extern __shared__ float smem[];
+    float* sm = smem;                    // [kWaves][16]
+    float* sl = sm + kWaves * 16;        // [kWaves][16]
+    float* so = sl + kWaves * 16;        // [kWaves][G][D]
+
+    const CacheArgs& c = p.c;
+    const DecodeArgs& a = p.a;
+    const int split = blockIdx.x;
+    const int grp = blockIdx.y;
+    const int s = grp / c.Hkv;
+    const int kvh = grp - s * c.Hkv;
+    const int G = c.G;
+    const int T = c.seq_lens[s];
+    const int U = a.cnt[grp] * TPB;
+    const int S = a.splits;
+    const int u0 = static_cast<int>(static_cast<int64_t>(U) * split / S);
+    const int u1 = static_cast<int>(static_cast<int64_t>(U) * (split + 1) / S);
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4;
+    const int col = lane & 15;
+
+    // B operand of S^T = K Q^T: lane (g, col) holds q[head col][32ks + 8g .. +8]
+    bf16x8 qb[KS];
+    {
+        const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
+                             (static_cast<int64_t>(s) * c.Hq + kvh * G + col) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            u32x4 w = {0u, 0u, 0u, 0u};
+            if (col < G) w = ldg16(qp + ks * 32 + g * 8);
+            qb[ks] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    floatx4 oacc[NT];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    const uint16_t* kpool = static_cast<const uint16_t*>(c.k_pool);
+    const uint16_t* vpool = static_cast<const uint16_t*>(c.v_pool);
+    const int32_t* idxrow = a.idx + static_cast<int64_t>(grp) * a.n_max;
+    const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
+    const float sl2 = a.scale_log2;
+
+    for (int u = u0 + wave; u < u1; u += kWaves) {
+        const int pi = u / TPB;
+        const int r = u - pi * TPB;
+        const int blk = idxrow[pi];
+        const int tok0 = blk * BLK + 32 * r;
+        const int nvalid = T - tok0;
+        if (nvalid <= 0) continue;  // tile past the end of a partial block
+        const int64_t page = ptrow[blk];
+        const int64_t toff = (page * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) + 32 * r * D;
+        const uint16_t* kt = kpool + toff + lane * 8;
+        const uint16_t* vt = vpool + toff + lane * 8;
+        u32x4 kr[2 * KS], vr[NT];
+#pragma unroll
+        for (int k = 0; k < 2 * KS; ++k) kr[k] = ldg16(kt + k * 512);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) vr[n] = ldg16(vt + n * 512);
+
+        // S^T for tokens [16mt, 16mt+16) x head columns
+        floatx4 sacc[2];
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    __builtin_bit_cast(bf16x8, kr[mt * KS + ks]), qb[ks], sacc[mt], 0, 0, 0);
+        }
+        float x[8];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int tok = (k < 4) ? (4 * g + k) : (16 + 4 * g + k - 4);
+            const float v = sacc[k >> 2][k & 3] * sl2;
+            x[k] = (tok < nvalid) ? v : -INFINITY;
+            tmax = fmaxf(tmax, x[k]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run, tmax);  // finite: token 0 of the tile is valid
+        const float alpha = exp2f(m_run - m_new);
+        float pr[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            pr[k] = exp2f(x[k] - m_new);
+            psum += pr[k];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        // O rows are heads 4g+e; their alpha lives in lane 4g+e
+        float al[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * g + e, 64);
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) oacc[n][e] *= al[e];
+
+        // P = hi + lo, both bf16
+        u32x4 phi, plo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint16_t h0 = f2bf(pr[2 * k]);
+            const uint16_t h1 = f2bf(pr[2 * k + 1]);
+            phi[k] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+            plo[k] = pack_bf2(pr[2 * k] - bf2f(h0), pr[2 * k + 1] - bf2f(h1));
+        }
+        if (nvalid < 32) {
+            // slots past the end may hold anything (even NaN): zero them
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int tok = (k < 4) ? (4 * g + k) : (16 + 4 * g + k - 4);
+                if (tok >= nvalid) {
+                    const uint32_t keep = (k & 1) ? 0x0000ffffu : 0xffff0000u;
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) vr[n][k >> 1] &= keep;
+                }
+            }
+        }
+        const bf16x8 ph = __builtin_bit_cast(bf16x8, phi);
+        const bf16x8 pl = __builtin_bit_cast(bf16x8, plo);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, vr[n]);
+            oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, oacc[n], 0, 0, 0);
+            oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[n], 0, 0, 0);
+        }
+    }
+
+    // per-wave totals: l summed over the 4 lane groups of each head column
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (g == 0) {
+        sm[wave * 16 + col] = m_run;
+        sl[wave * 16 + col] = l_tot;
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int h = 4 * g + e;
+        if (h < G) {
+#pragma unroll
+            for (int n = 0; n < NT; ++n) so[(wave * G + h) * D + n * 16 + col] = oacc[n][e];
+        }
+    }
+    __syncthreads();
+    merge_waves_and_store(sm, sl, so, G, D, a.o_part, a.lse_part,
+                          static_cast<int64_t>(s) * c.Hq + kvh * G, S, split);
+}
+
+// fp32 caches: same split, plain arithmetic.  Lane t < 32 owns token t of a
+// tile for the logits; every lane owns channels lane, lane+64 for O.
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeParams p) {
+    constexpr int CPL = D / 64;  // output channels per lane
+    extern __shared__ float smem[];
+    float* sm = smem;
+    float* sl = sm + kWaves * 16;
+    float* so = sl + kWaves * 16;  // [kWaves][G][D]
+    float* qs = so + kWaves * p.c.G * D;  // [G][D]
+
+    const CacheArgs& c = p.c;
+    const DecodeArgs& a = p.a;
+    const int split = blockIdx.x;
+    const int grp = blockIdx.y;
+    const int s = grp / c.Hkv;
+    const int kvh = grp - s * c.Hkv;
+    const int G = c.G;
+    const int T = c.seq_lens[s];
+    const int BLK = c.block;
+    const int TPB = BLK / 32;
+    const int U = a.cnt[grp] * TPB;
+    const int S = a.splits;
+    const int u0 = static_cast<int>(static_cast<int64_t>(U) * split / S);
+    const int u1 = static_cast<int>(static_cast<int64_t>(U) * (split + 1) / S);
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+
+    const float* qg = static_cast<const float*>(a.q) + (static_cast<int64_t>(s) * c.Hq + kvh * G) * D;
+    for (int k = threadIdx.x; k < G * D; k += kThreads) qs[k] = qg[k];
+    __syncthreads();
+
+    float m[16], l[16], o[16][CPL];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+        m[h] = -INFINITY;
+        l[h] = 0.f;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) o[h][k] = 0.f;
+    }
+    const float* kpool = static_cast<const float*>(c.k_pool);
+    const float* vpool = static_cast<const float*>(c.v_pool);
+    const int32_t* idxrow = a.idx + static_cast<int64_t>(grp) * a.n_max;
+    const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
+
+    for (int u = u0 + wave; u < u1; u += kWaves) {
+        const int pi = u / TPB;
+        const int r = u - pi * TPB;
+        const int blk = idxrow[pi];
+        const int tok0 = blk * BLK + 32 * r;
+        const int nvalid = min(32, T - tok0);
+        if (nvalid <= 0) continue;
+        const int64_t page = ptrow[blk];
+        const float* kt = kpool + (page * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) + 32 * r * D;
+        const float* vt = vpool + (page * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) + 32 * r * D;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+            if (h >= G) continue;  // (not break: keeps the loop unrollable)
+            float z = -INFINITY;
+            if (lane < nvalid) {
+                float acc = 0.f;
+                for (int i = 0; i < D; ++i) acc += qs[h * D + i] * kt[lane * D + i];
+                z = acc * a.scale_log2;
+            }
+            const float mt = wave_max(z);
+            const float m_new = fmaxf(m[h], mt);
+            const float alpha = exp2f(m[h] - m_new);
+            const float pz = (lane < nvalid) ? exp2f(z - m_new) : 0.f;
+            l[h] = l[h] * alpha + wave_sum(pz);
+            m[h] = m_new;
+#pragma unroll
+            for (int k = 0; k < CPL; ++k) {
+                const int ch = lane + 64 * k;
+                float acc = o[h][k] * alpha;
+                for (int t = 0; t < nvalid; ++t) acc += __shfl(pz, t, 64) * vt[t * D + ch];
+                o[h][k] = acc;
+            }
+        }
+    }
+    if (lane < 16) {
+        float mv = -INFINITY, lv = 0.f;
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+            if (h == lane) {
+                mv = m[h];
+                lv = l[h];
+            }
+        sm[wave * 16 + lane] = mv;
+        sl[wave * 16 + lane] = lv;
+    }
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+        if (h >= G) continue;
+#pragma unroll
+        for (int k = 0; k < CPL; ++k) so[(wave * G + h) * D + lane + 64 * k] = o[h][k];
+    }
+    __syncthreads();
+    merge_waves_and_store(sm, sl, so, G, D, a.o_part, a.lse_part,
+                          static_cast<int64_t>(s) * c.Hq + kvh * G, S, split);
+}
+
+// Merge of the partial (o, base-2 lse) pairs of each row, in fixed split
+// order.  Row `row` merges its first S splits, or, when seq_lens is given,
+// only the splits that cover [0, seq_lens[row / rows_per_seq]) at
+// tokens_per_split tokens each (the others were never written).
+template <int DT>
+__global__ void combine_kernel(int d, int S, const float* __restrict__ o_part,
+                               const float* __restrict__ lse_part, void* o, float* lse,
+                               const int32_t* seq_lens, int rows_per_seq, int tokens_per_split) {
+    const int64_t row = blockIdx.x;
+    int Sv = S;
+    if (seq_lens) {
+        const int T = seq_lens[row / rows_per_seq];
+        Sv = min(S, (T + tokens_per_split - 1) / tokens_per_split);
+    }
+    const float* lp = lse_part + row * S;
+    float M = -INFINITY;
+    for (int k = 0; k < Sv; ++k) M = fmaxf(M, lp[k]);
+    for (int ch = threadIdx.x; ch < d; ch += blockDim.x) {
+        float val = 0.f;
+        if (M != -INFINITY) {
+            float L = 0.f, acc = 0.f;
+            for (int k = 0; k < Sv; ++k) {
+                const float w = exp2f(lp[k] - M);
+                L += w;
+                acc += w * o_part[(row * S + k) * d + ch];
+            }
+            val = acc / L;
+            if (ch == 0) lse[row] = (M + log2f(L)) * kLn2;
+        } else if (ch == 0) {
+            lse[row] = -INFINITY;
+        }
+        Elem<DT>::store(static_cast<typename Elem<DT>::T*>(o), row * d + ch, val);
+    }
+}
+
+template <int D, int BLK>
+hipError_t launch_bf16(const DecodeParams& p, hipStream_t stream) {
+    const size_t shm = sizeof(float) * (2 * kWaves * 16 + kWaves * p.c.G * D);
+    dim3 grid(p.a.splits, p.c.B * p.c.Hkv);
+    hipLaunchKernelGGL((decode_bf16_kernel<D, BLK>), grid, dim3(kThreads), shm, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bf16_d(const DecodeParams& p, hipStream_t stream) {
+    switch (p.c.block) {
+        case 32: return launch_bf16<D, 32>(p, stream);
+        case 64: return launch_bf16<D, 64>(p, stream);
+        case 128: return launch_bf16<D, 128>(p, stream);
+        case 256: return launch_bf16<D, 256>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int D>
+hipError_t launch_f32(const DecodeParams& p, hipStream_t stream) {
+    const size_t shm = sizeof(float) * (2 * kWaves * 16 + kWaves * p.c.G * D + p.c.G * D);
+    dim3 grid(p.a.splits, p.c.B * p.c.Hkv);
+    hipLaunchKernelGGL((decode_f32_kernel<D>), grid, dim3(kThreads), shm, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_splits(const CacheArgs& c, int n_max) {
+    // ~1024 workgroups over the chip (4 per CU), at least 4 tiles (one per
+    // wave) in every split.
+    const int groups = c.B * c.Hkv;
+    const int tiles = n_max * (c.block / 32);
+    int S = (1024 + groups - 1) / groups;
+    const int cap = (tiles + 3) / 4;
+    if (S > cap) S = cap;
+    if (S < 1) S = 1;
+    return S;
+}
+
+hipError_t launch_combine_ragged(int dtype, int d, int rows, int splits, const float* o_part,
+                                 const float* lse_part, void* o, float* lse,
+                                 const int32_t* seq_lens, int rows_per_seq,
+                                 int tokens_per_split, hipStream_t stream) {
+    const int threads = d;
+    if (dtype == kBF16)
+        hipLaunchKernelGGL((combine_kernel<kBF16>), dim3(rows), dim3(threads), 0, stream, d, splits,
+                           o_part, lse_part, o, lse, seq_lens, rows_per_seq, tokens_per_split);
+    else
+        hipLaunchKernelGGL((combine_kernel<kF32>), dim3(rows), dim3(threads), 0, stream, d, splits,
+                           o_part, lse_part, o, lse, seq_lens, rows_per_seq, tokens_per_split);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(int dtype, int d, int rows, int splits, const float* o_part,
+                          const float* lse_part, void* o, float* lse, hipStream_t stream) {
+    return launch_combine_ragged(dtype, d, rows, splits, o_part, lse_part, o, lse, nullptr, 1, 1,
+                                 stream);
+}
+
+hipError_t launch_decode(const CacheArgs& c, const DecodeArgs& a, hipStream_t stream) {
+    DecodeParams p{c, a};
+    hipError_t err;
+    if (c.dtype == kBF16)
+        err = c.d == 64 ? launch_bf16_d<64>(p, stream) : launch_bf16_d<128>(p, stream);
+    else
+        err = c.d == 64 ? launch_f32<64>(p, stream) : launch_f32<128>(p, stream);
+    if (err != hipSuccess) return err;
+    return launch_combine(c.dtype, c.d, c.B * c.Hq, a.splits, a.o_part, a.lse_part, a.o, a.lse,
+                          stream);
+}
+
+}  // namespace bsa

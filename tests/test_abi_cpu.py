@@ -1,0 +1,166 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/bsa.h declares, and rejects bad arguments with the documented
+status before making any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_build_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"BSA_API\s+[\w\s\*]+?\b(bsa_\w+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["bsa_build_block_desc", "bsa_select_blocks", "bsa_sparse_decode",
+              "bsa_rectify_chunk", "bsa_workspace_size", "bsa_status_string",
+              "bsa_block_count"]:
+        assert n in names
+    assert sorted(bsa.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    L = bsa.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_no_internal_symbols_exported():
+    # only the C entry points are visible from the shared object
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", bsa._LIBPATH], capture_output=True,
+                         text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert {s for s in syms if s.startswith("bsa_")} == set(declared_functions())
+    assert not any("launch_" in s for s in syms)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert bsa.status_string(s)
+    assert bsa.status_string(99) == "unknown status"
+
+
+def L_ok(**kw):
+    base = dict(B=2, Hq=32, Hkv=8, d=128, block=64, max_blocks=100,
+                kv_dtype=bsa.DTYPE_BF16, desc_kind=bsa.DESC_MINMAX)
+    base.update(kw)
+    return bsa.Layout(**base)
+
+
+def test_workspace_size():
+    L = L_ok()
+    assert bsa.workspace_size(L, bsa.OP_SELECT, 10) >= 2 * 8 * 100 * 4
+    assert bsa.workspace_size(L, bsa.OP_DECODE, 10) > 2 * 32 * 128 * 4
+    assert bsa.workspace_size(L, bsa.OP_RECTIFY, 32) > 2 * 32 * 32 * 128 * 4
+    assert bsa.workspace_size(L, 99, 10) == 0
+    assert bsa.workspace_size(L_ok(d=96), bsa.OP_DECODE, 10) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=30), bsa.ERR_SHAPE),
+    (dict(B=0), bsa.ERR_SHAPE),
+    (dict(d=96), bsa.ERR_UNSUPPORTED),
+    (dict(block=48), bsa.ERR_UNSUPPORTED),
+    (dict(kv_dtype=7), bsa.ERR_UNSUPPORTED),
+    (dict(desc_kind=3), bsa.ERR_UNSUPPORTED),
+    (dict(Hq=8 * 32), bsa.ERR_UNSUPPORTED),        # G = 32 > 16
+    (dict(max_blocks=40000), bsa.ERR_UNSUPPORTED),
+])
+def test_layout_rejected_before_any_hip_call(kw, status):
+    L = L_ok(**kw)
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    C = bsa.c_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    st = bsa.lib().bsa_build_block_desc(ctypes.byref(L.c()), ctypes.byref(C), fake, fake, 1,
+                                        None, None)
+    assert st == status
+
+
+def _select(L, P, ws_bytes=1 << 30, q=0x1000, cache_ptr=0x1000):
+    C = bsa.c_cache(cache_ptr, 0x1000, 0x1000, 0x1000, 0x1000)
+    p = ctypes.c_void_p(0x1000)
+    return bsa.lib().bsa_select_blocks(ctypes.byref(L.c()), ctypes.byref(C),
+                                       ctypes.c_void_p(q) if q else None,
+                                       ctypes.byref(P.c()), p, p, p, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_local=0), bsa.ERR_PARAM),
+    (dict(n_min=-1), bsa.ERR_PARAM),
+    (dict(budget_tokens=-5), bsa.ERR_PARAM),
+    (dict(sparsity_bp=10000), bsa.ERR_PARAM),
+    (dict(sparsity_bp=-1), bsa.ERR_PARAM),
+    (dict(n_max=5), bsa.ERR_PARAM),                 # needs 10 for NB = 100, p = 0.9
+])
+def test_select_params_rejected(kw, status):
+    base = dict(sparsity_bp=9000, n_local=2, n_min=0, n_max=10)
+    base.update(kw)
+    assert _select(L_ok(), bsa.SelectParams(**base)) == status
+
+
+def test_select_null_and_workspace():
+    P = bsa.SelectParams(sparsity_bp=9000, n_local=2, n_max=10)
+    assert _select(L_ok(), P, q=0) == bsa.ERR_NULL
+    assert _select(L_ok(), P, cache_ptr=0) == bsa.ERR_NULL
+    assert _select(L_ok(), P, ws_bytes=16) == bsa.ERR_WORKSPACE
+    # mean-pool descriptors need a gate weight
+    assert _select(L_ok(desc_kind=bsa.DESC_MEANPOOL), P) == bsa.ERR_PARAM
+
+
+def test_decode_and_rectify_validation():
+    L = L_ok()
+    C = bsa.c_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    p = ctypes.c_void_p(0x1000)
+    lib = bsa.lib()
+    st = lib.bsa_sparse_decode(ctypes.byref(L.c()), ctypes.byref(C), p, p, p, 10, 0.0, p, p, p,
+                               1 << 30, None)
+    assert st == bsa.ERR_PARAM  # scale must be > 0
+    st = lib.bsa_sparse_decode(ctypes.byref(L.c()), ctypes.byref(C), p, p, p, 10, float("nan"),
+                               p, p, p, 1 << 30, None)
+    assert st == bsa.ERR_PARAM
+    st = lib.bsa_sparse_decode(ctypes.byref(L.c()), ctypes.byref(C), p, p, p, 10, 0.1, p, p, p,
+                               64, None)
+    assert st == bsa.ERR_WORKSPACE
+    st = lib.bsa_sparse_decode(ctypes.byref(L.c()), ctypes.byref(C), p, None, p, 10, 0.1, p, p,
+                               p, 1 << 30, None)
+    assert st == bsa.ERR_NULL
+    st = lib.bsa_rectify_chunk(ctypes.byref(L.c()), ctypes.byref(C), p, p, p, 0, 0.1, p, p, p,
+                               1 << 30, None)
+    assert st == bsa.ERR_PARAM
+    st = lib.bsa_rectify_chunk(ctypes.byref(L.c()), ctypes.byref(C), p, p, p, 32, 0.1, p, p, p,
+                               1024, None)
+    assert st == bsa.ERR_WORKSPACE
+    st = lib.bsa_rectify_chunk(ctypes.byref(L.c()), ctypes.byref(C), p, p, p, 32 * 100 * 64,
+                               0.1, p, p, p, 1 << 40, None)
+    assert st == bsa.ERR_PARAM   # f beyond the capacity
+
+
+def test_build_block_desc_argument_rules():
+    L = L_ok()
+    C = bsa.c_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    p = ctypes.c_void_p(0x1000)
+    lib = bsa.lib()
+    assert lib.bsa_build_block_desc(ctypes.byref(L.c()), ctypes.byref(C), p, None, 1, None,
+                                    None) == bsa.ERR_PARAM
+    assert lib.bsa_build_block_desc(ctypes.byref(L.c()), ctypes.byref(C), p, p, 0, None,
+                                    None) == bsa.ERR_PARAM
+    assert lib.bsa_build_block_desc(ctypes.byref(L.c()), ctypes.byref(C), p, p, 1, p,
+                                    None) == bsa.ERR_PARAM
+    assert lib.bsa_build_block_desc(None, ctypes.byref(C), p, p, 1, None, None) == bsa.ERR_NULL
+
+
+def test_host_block_count_matches_oracle():
+    import oracle as O
+    for budget, bp, nl, nm in [(512, 0, 1, 2), (4096, 0, 1, 0), (0, 9000, 2, 16),
+                               (0, 9500, 2, 16), (0, 9800, 2, 0), (0, 0, 1, 0)]:
+        P = bsa.SelectParams(budget_tokens=budget, sparsity_bp=bp, n_local=nl, n_min=nm)
+        for NB in [1, 2, 5, 33, 257, 513, 2049, 8193]:
+            assert bsa.block_count(P, NB, 64) == O.block_count(NB, 64, budget, bp, nl, nm)
