@@ -216,7 +216,10 @@ def enforce_gap(L, params, q, Ks, lengths_per_step, W_gate=None, rel=1e-3, max_i
                         u.astype(np.float64),
                         (qg.astype(np.float64).sum(0) if L.desc_kind == bsa.DESC_MINMAX
                          else W_gate.astype(np.float64) @ qg.astype(np.float64).sum(0))))
-                    delta = 3.0 * (need - (s_in - s_out)) / grad + 1e-2
+                    # at least a few storage ulps per channel: the min/max entries
+                    # are the largest-magnitude keys, and smaller shifts of them
+                    # round away in bf16
+                    delta = max(4.0 * (need - (s_in - s_out)) / grad, 0.25 * (1 + it))
                     for j in order[:k]:
                         t0, t1 = j * b, (j + 1) * b
                         Ks[s][h, t0:t1] = W.quantize(Ks[s][h, t0:t1] + delta * u,
