@@ -89,7 +89,7 @@ RectifyWs rectify_ws(const CacheArgs& c, int f) {
 }
 
 size_t select_ws(const CacheArgs& c) {
-    return align_up(static_cast<size_t>(c.B) * c.Hkv * c.max_blocks * sizeof(float));
+    return align_up(static_cast<size_t>(c.B) * c.Hkv * score_stride(c.max_blocks) * sizeof(float));
 }
 
 bsa_status check_select_params(const bsa_layout* L, const bsa_select_params* P) {

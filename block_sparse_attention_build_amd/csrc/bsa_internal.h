@@ -32,11 +32,13 @@ struct SelectArgs {
     int budget_tokens, sparsity_bp, n_local, n_min, n_max;
     int32_t* idx;
     int32_t* cnt;
-    float* scores;  // workspace [B*Hkv][max_blocks]
+    float* scores;  // workspace [B*Hkv][score_stride(max_blocks)]
 };
 hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t stream);
 // keys-per-thread bucket of the top-n kernel for a given max_blocks (0 = too many)
 int topn_keys_per_thread(int max_blocks);
+// row stride (floats) of the score workspace: max_blocks rounded up to 4
+int score_stride(int max_blocks);
 
 struct DecodeArgs {
     const void* q;

@@ -38,9 +38,19 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
+// Tuning: waves per SIMD the bf16 kernel is register-limited to, and the
+// number of workgroups a decode call aims for (one resident round on 256 CUs).
+#ifndef BSA_DECODE_WAVES_PER_EU
+#define BSA_DECODE_WAVES_PER_EU 2
+#endif
+#ifndef BSA_DECODE_TARGET_WGS
+#define BSA_DECODE_TARGET_WGS 512
+#endif
+
 struct DecodeParams {
     CacheArgs c;
     DecodeArgs a;
+    int max_blocks_per_wg;  // LDS slots for a split's block/page ids
 };
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
@@ -79,7 +89,9 @@ __device__ __forceinline__ void merge_waves_and_store(const float* sm, const flo
 }
 
 template <int D, int BLK>
-__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf16_kernel(
+    DecodeParams p) {
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int NT = D / 16;   // column tiles of the PV product
     constexpr int TPB = BLK / 32;
@@ -87,6 +99,8 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
     float* sm = smem;                    // [kWaves][16]
     float* sl = sm + kWaves * 16;        // [kWaves][16]
     float* so = sl + kWaves * 16;        // [kWaves][G][D]
+    int* s_blk = reinterpret_cast<int*>(so + kWaves * p.c.G * D);  // [max_blocks_per_wg]
+    int* s_page = s_blk + p.max_blocks_per_wg;                      // [max_blocks_per_wg]
 
     const CacheArgs& c = p.c;
     const DecodeArgs& a = p.a;
@@ -95,9 +109,11 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
     const int s = grp / c.Hkv;
     const int kvh = grp - s * c.Hkv;
     const int G = c.G;
-    const int T = c.seq_lens[s];
-    const int U = a.cnt[grp] * TPB;
     const int S = a.splits;
+    // The split ranges cover n_max blocks (known before any load), so the
+    // block ids, the kept count, the length and the queries are requested
+    // together; entries at or past cnt are empty tiles.
+    const int U = a.n_max * TPB;
     const int u0 = static_cast<int>(static_cast<int64_t>(U) * split / S);
     const int u1 = static_cast<int>(static_cast<int64_t>(U) * (split + 1) / S);
     const int wave = threadIdx.x >> 6;
@@ -118,6 +134,22 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
         }
     }
 
+    // block ids and page ids of this split, resolved once (two dependent
+    // round trips for the whole workgroup instead of two per tile)
+    const int32_t* idxrow = a.idx + static_cast<int64_t>(grp) * a.n_max;
+    const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
+    const int pb0 = u0 / TPB;
+    const int nblk = (u1 > u0) ? (u1 - 1) / TPB - pb0 + 1 : 0;
+    const int cnt = a.cnt[grp];
+    const int T = c.seq_lens[s];
+    for (int i = threadIdx.x; i < nblk; i += kThreads) {
+        const int blk = idxrow[pb0 + i];
+        const bool kept = pb0 + i < cnt;
+        s_blk[i] = kept ? blk : (T / BLK + 1);  // an empty tile: starts past T
+        s_page[i] = kept ? ptrow[blk] : 0;
+    }
+    __syncthreads();
+
     floatx4 oacc[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -126,28 +158,42 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
 
     const uint16_t* kpool = static_cast<const uint16_t*>(c.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(c.v_pool);
-    const int32_t* idxrow = a.idx + static_cast<int64_t>(grp) * a.n_max;
-    const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
     const float sl2 = a.scale_log2;
 
-    for (int u = u0 + wave; u < u1; u += kWaves) {
+    // This wave's tiles: a contiguous, balanced share of the split, clipped
+    // to the kept count.  The loop is software-pipelined: the next tile's K
+    // loads are issued as soon as QK has consumed the current K registers,
+    // and its V loads as soon as PV has consumed V.  The steady-state body
+    // has no branch around a load (the last tile is a separate copy without
+    // next-tile loads; tiles past the end of a partial block are loaded and
+    // fully masked), so the compiler's wait counters only wait for the
+    // registers each step needs.  Tile addressing is wave-uniform.
+    const int per = u1 - u0;
+    const int w0 = u0 + per * wave / kWaves;
+    const int w1 = min(u0 + per * (wave + 1) / kWaves, cnt * TPB);
+    const uint16_t* kl = kpool + lane * 8;
+    const uint16_t* vl = vpool + lane * 8;
+    u32x4 kr[2 * KS], vr[NT];
+    // tile u -> (element offset of its 32-token run, tokens valid in it)
+    auto resolve = [&](int u, int64_t& off, int& nvalid) __attribute__((always_inline)) {
         const int pi = u / TPB;
         const int r = u - pi * TPB;
-        const int blk = idxrow[pi];
-        const int tok0 = blk * BLK + 32 * r;
-        const int nvalid = T - tok0;
-        if (nvalid <= 0) continue;  // tile past the end of a partial block
-        const int64_t page = ptrow[blk];
-        const int64_t toff = (page * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) + 32 * r * D;
-        const uint16_t* kt = kpool + toff + lane * 8;
-        const uint16_t* vt = vpool + toff + lane * 8;
-        u32x4 kr[2 * KS], vr[NT];
+        const int blk = __builtin_amdgcn_readfirstlane(s_blk[pi - pb0]);
+        const int page = __builtin_amdgcn_readfirstlane(s_page[pi - pb0]);
+        nvalid = T - (blk * BLK + 32 * r);
+        off = (static_cast<int64_t>(page) * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) + 32 * r * D;
+    };
+    auto load_k = [&](int64_t off) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < 2 * KS; ++k) kr[k] = ldg16(kt + k * 512);
+        for (int k = 0; k < 2 * KS; ++k) kr[k] = ldg16(kl + off + k * 512);
+    };
+    auto load_v = [&](int64_t off) __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) vr[n] = ldg16(vt + n * 512);
-
-        // S^T for tokens [16mt, 16mt+16) x head columns
+        for (int n = 0; n < NT; ++n) vr[n] = ldg16(vl + off + n * 512);
+    };
+    // one tile: QK, online softmax, PV; NEXT: also issue tile u+1's loads
+    auto step = [&](const int nvalid, const bool next, const int64_t off_nxt)
+                    __attribute__((always_inline)) {
         floatx4 sacc[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -157,66 +203,74 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeParams p) {
                 sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                     __builtin_bit_cast(bf16x8, kr[mt * KS + ks]), qb[ks], sacc[mt], 0, 0, 0);
         }
+        if (next) load_k(off_nxt);
         float x[8];
-        float tmax = -INFINITY;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int tok = (k < 4) ? (4 * g + k) : (16 + 4 * g + k - 4);
-            const float v = sacc[k >> 2][k & 3] * sl2;
-            x[k] = (tok < nvalid) ? v : -INFINITY;
-            tmax = fmaxf(tmax, x[k]);
+            x[k] = (tok < nvalid) ? sacc[k >> 2][k & 3] * sl2 : -INFINITY;
         }
+        float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                           fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax);  // finite: token 0 of the tile is valid
-        const float alpha = exp2f(m_run - m_new);
-        float pr[8];
-        float psum = 0.f;
+        if (__ballot(tmax > m_run) != 0) {  // some head's running max grows
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+            l_run *= alpha;
+            m_run = m_new;
+            // O rows are heads 4g+e; their alpha lives in lane 4g+e
+            float al[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            pr[k] = exp2f(x[k] - m_new);
-            psum += pr[k];
+            for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * g + e, 64);
+#pragma unroll
+            for (int n = 0; n < NT; ++n)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) oacc[n][e] *= al[e];
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        // O rows are heads 4g+e; their alpha lives in lane 4g+e
-        float al[4];
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // nothing seen yet
+        float pr[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * g + e, 64);
+        for (int k = 0; k < 8; ++k) pr[k] = __builtin_amdgcn_exp2f(x[k] - m_use);
+        l_run += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+        // P = hi + lo, both bf16 (round to nearest even in hardware)
+        bf16x8 ph, pl;
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
+        for (int k = 0; k < 8; ++k) ph[k] = static_cast<__bf16>(pr[k]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) oacc[n][e] *= al[e];
-
-        // P = hi + lo, both bf16
-        u32x4 phi, plo;
+        for (int k = 0; k < 8; ++k) pl[k] = static_cast<__bf16>(pr[k] - static_cast<float>(ph[k]));
+        // token slots past the end may hold anything (even NaN): zero them
+        uint32_t keep[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint16_t h0 = f2bf(pr[2 * k]);
-            const uint16_t h1 = f2bf(pr[2 * k + 1]);
-            phi[k] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-            plo[k] = pack_bf2(pr[2 * k] - bf2f(h0), pr[2 * k + 1] - bf2f(h1));
+            const int t0 = (2 * k < 4) ? (4 * g + 2 * k) : (16 + 4 * g + 2 * k - 4);
+            keep[k] = (t0 < nvalid ? 0x0000ffffu : 0u) | (t0 + 1 < nvalid ? 0xffff0000u : 0u);
         }
-        if (nvalid < 32) {
-            // slots past the end may hold anything (even NaN): zero them
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int tok = (k < 4) ? (4 * g + k) : (16 + 4 * g + k - 4);
-                if (tok >= nvalid) {
-                    const uint32_t keep = (k & 1) ? 0x0000ffffu : 0xffff0000u;
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) vr[n][k >> 1] &= keep;
-                }
-            }
-        }
-        const bf16x8 ph = __builtin_bit_cast(bf16x8, phi);
-        const bf16x8 pl = __builtin_bit_cast(bf16x8, plo);
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
-            const bf16x8 vb = __builtin_bit_cast(bf16x8, vr[n]);
+            u32x4 vm = vr[n];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) vm[k] &= keep[k];
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, vm);
             oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, oacc[n], 0, 0, 0);
             oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[n], 0, 0, 0);
         }
+        if (next) load_v(off_nxt);
+    };
+    if (w0 < w1) {
+        int64_t off = 0;
+        int nv = 0;
+        resolve(w0, off, nv);
+        load_k(off);
+        load_v(off);
+        for (int u = w0; u + 1 < w1; ++u) {
+            int64_t off_nxt = 0;
+            int nv_nxt = 0;
+            resolve(u + 1, off_nxt, nv_nxt);
+            step(nv, true, off_nxt);
+            nv = nv_nxt;
+        }
+        step(nv, false, 0);
     }
 
     // per-wave totals: l summed over the 4 lane groups of each head column
@@ -340,44 +394,86 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeParams p) {
                           static_cast<int64_t>(s) * c.Hq + kvh * G, S, split);
 }
 
-// Merge of the partial (o, base-2 lse) pairs of each row, in fixed split
-// order.  Row `row` merges its first S splits, or, when seq_lens is given,
-// only the splits that cover [0, seq_lens[row / rows_per_seq]) at
-// tokens_per_split tokens each (the others were never written).
+// Merge of the partial (o, base-2 lse) pairs of each row, in a fixed order.
+// Row `row` merges its first S splits, or, when seq_lens is given, only the
+// splits that cover [0, seq_lens[row / rows_per_seq]) at tokens_per_split
+// tokens each (the others were never written).  Grid: rows x (d / 64); a
+// workgroup puts the split weights 2^(lse_k - M) in LDS, then its 256 threads
+// take 64 channels x 4 split lanes, each lane summing every 4th split with 8
+// independent loads in flight, and the 4 lane sums are added in fixed order.
+constexpr int kCombThreads = 256;
+constexpr int kCombCh = 64;                        // channels per workgroup
+constexpr int kCombLanes = kCombThreads / kCombCh;  // split lanes per channel
+
 template <int DT>
-__global__ void combine_kernel(int d, int S, const float* __restrict__ o_part,
-                               const float* __restrict__ lse_part, void* o, float* lse,
-                               const int32_t* seq_lens, int rows_per_seq, int tokens_per_split) {
+__global__ __launch_bounds__(kCombThreads) void combine_kernel(
+    int d, int S, const float* __restrict__ o_part, const float* __restrict__ lse_part, void* o,
+    float* lse, const int32_t* seq_lens, int rows_per_seq, int tokens_per_split) {
+    extern __shared__ float wts[];  // [S] weights
+    __shared__ float red[kCombThreads / kWave];
+    __shared__ float part_sum[kCombLanes][kCombCh];
     const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
     int Sv = S;
     if (seq_lens) {
         const int T = seq_lens[row / rows_per_seq];
         Sv = min(S, (T + tokens_per_split - 1) / tokens_per_split);
     }
     const float* lp = lse_part + row * S;
+    float m = -INFINITY;
+    for (int k = tid; k < Sv; k += kCombThreads) {
+        const float v = lp[k];
+        wts[k] = v;
+        m = fmaxf(m, v);
+    }
+    m = wave_max(m);
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
     float M = -INFINITY;
-    for (int k = 0; k < Sv; ++k) M = fmaxf(M, lp[k]);
-    for (int ch = threadIdx.x; ch < d; ch += blockDim.x) {
-        float val = 0.f;
-        if (M != -INFINITY) {
-            float L = 0.f, acc = 0.f;
-            for (int k = 0; k < Sv; ++k) {
-                const float w = exp2f(lp[k] - M);
-                L += w;
-                acc += w * o_part[(row * S + k) * d + ch];
-            }
-            val = acc / L;
-            if (ch == 0) lse[row] = (M + log2f(L)) * kLn2;
-        } else if (ch == 0) {
-            lse[row] = -INFINITY;
-        }
-        Elem<DT>::store(static_cast<typename Elem<DT>::T*>(o), row * d + ch, val);
+#pragma unroll
+    for (int w = 0; w < kCombThreads / kWave; ++w) M = fmaxf(M, red[w]);
+    __syncthreads();
+    float lsum = 0.f;
+    for (int k = tid; k < Sv; k += kCombThreads) {
+        const float wk = (M == -INFINITY) ? 0.f : exp2f(wts[k] - M);
+        wts[k] = wk;
+        lsum += wk;
+    }
+    lsum = wave_sum(lsum);
+    if ((tid & 63) == 0) red[tid >> 6] = lsum;
+    __syncthreads();
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kCombThreads / kWave; ++w) L += red[w];
+    const int cl = tid % kCombCh;
+    const int lane_k = tid / kCombCh;
+    const int ch = blockIdx.y * kCombCh + cl;
+    const float* op = o_part + row * S * d + ch;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int k = lane_k;
+    for (; k + 7 * kCombLanes < Sv; k += 8 * kCombLanes) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            acc[u] += wts[k + u * kCombLanes] * op[static_cast<int64_t>(k + u * kCombLanes) * d];
+    }
+    for (; k < Sv; k += kCombLanes) acc[0] += wts[k] * op[static_cast<int64_t>(k) * d];
+    part_sum[lane_k][cl] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) +
+                           ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    __syncthreads();
+    if (lane_k == 0) {
+        float tot = 0.f;
+#pragma unroll
+        for (int p2 = 0; p2 < kCombLanes; ++p2) tot += part_sum[p2][cl];
+        const bool empty = (M == -INFINITY);
+        Elem<DT>::store(static_cast<typename Elem<DT>::T*>(o), row * d + ch, empty ? 0.f : tot / L);
+        if (ch == 0) lse[row] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
     }
 }
 
 template <int D, int BLK>
 hipError_t launch_bf16(const DecodeParams& p, hipStream_t stream) {
-    const size_t shm = sizeof(float) * (2 * kWaves * 16 + kWaves * p.c.G * D);
+    const size_t shm = sizeof(float) * (2 * kWaves * 16 + kWaves * p.c.G * D) +
+                       2 * sizeof(int) * p.max_blocks_per_wg;
     dim3 grid(p.a.splits, p.c.B * p.c.Hkv);
     hipLaunchKernelGGL((decode_bf16_kernel<D, BLK>), grid, dim3(kThreads), shm, stream, p);
     return hipGetLastError();
@@ -405,11 +501,11 @@ hipError_t launch_f32(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 int decode_splits(const CacheArgs& c, int n_max) {
-    // ~1024 workgroups over the chip (4 per CU), at least 4 tiles (one per
-    // wave) in every split.
+    // about BSA_DECODE_TARGET_WGS workgroups over the chip, at least 4 tiles
+    // (one per wave) in every split.
     const int groups = c.B * c.Hkv;
     const int tiles = n_max * (c.block / 32);
-    int S = (1024 + groups - 1) / groups;
+    int S = (BSA_DECODE_TARGET_WGS + groups - 1) / groups;
     const int cap = (tiles + 3) / 4;
     if (S > cap) S = cap;
     if (S < 1) S = 1;
@@ -420,13 +516,16 @@ hipError_t launch_combine_ragged(int dtype, int d, int rows, int splits, const f
                                  const float* lse_part, void* o, float* lse,
                                  const int32_t* seq_lens, int rows_per_seq,
                                  int tokens_per_split, hipStream_t stream) {
-    const int threads = d;
+    const size_t shm = sizeof(float) * static_cast<size_t>(splits);
+    const dim3 grid(rows, d / kCombCh);
     if (dtype == kBF16)
-        hipLaunchKernelGGL((combine_kernel<kBF16>), dim3(rows), dim3(threads), 0, stream, d, splits,
-                           o_part, lse_part, o, lse, seq_lens, rows_per_seq, tokens_per_split);
+        hipLaunchKernelGGL((combine_kernel<kBF16>), grid, dim3(kCombThreads), shm, stream, d,
+                           splits, o_part, lse_part, o, lse, seq_lens, rows_per_seq,
+                           tokens_per_split);
     else
-        hipLaunchKernelGGL((combine_kernel<kF32>), dim3(rows), dim3(threads), 0, stream, d, splits,
-                           o_part, lse_part, o, lse, seq_lens, rows_per_seq, tokens_per_split);
+        hipLaunchKernelGGL((combine_kernel<kF32>), grid, dim3(kCombThreads), shm, stream, d,
+                           splits, o_part, lse_part, o, lse, seq_lens, rows_per_seq,
+                           tokens_per_split);
     return hipGetLastError();
 }
 
@@ -437,7 +536,11 @@ hipError_t launch_combine(int dtype, int d, int rows, int splits, const float* o
 }
 
 hipError_t launch_decode(const CacheArgs& c, const DecodeArgs& a, hipStream_t stream) {
-    DecodeParams p{c, a};
+    // a split covers at most ceil(n_max*TPB / S) tiles, which touch at most
+    // that many / TPB + 1 blocks (+1 more when it starts inside a block)
+    const int tpb = c.block / 32;
+    const int tiles = (a.n_max * tpb + a.splits - 1) / a.splits;
+    DecodeParams p{c, a, tiles / tpb + 2};
     hipError_t err;
     if (c.dtype == kBF16)
         err = c.d == 64 ? launch_bf16_d<64>(p, stream) : launch_bf16_d<128>(p, stream);

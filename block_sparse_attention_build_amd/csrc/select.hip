@@ -40,6 +40,7 @@ constexpr int kTopnWaves = kTopnThreads / kWave;
 struct ScoreParams {
     CacheArgs c;
     SelectArgs s;
+    int stride;  // score row stride (floats)
 };
 
 // 16-byte chunk of descriptor elements as floats
@@ -67,50 +68,82 @@ struct Chunk<kF32> {
     }
 };
 
+// Descriptor row geometry: BR bytes per block (both rows for min/max), read
+// as 16-byte pieces, LPB = BR/16 lanes per block, so that one wave load
+// instruction covers 64/LPB whole blocks = one contiguous KiB.  A lane of a
+// min/max block owns 8 (bf16) or 4 (fp32) channels of either the min row
+// (paired with Q-) or the max row (paired with Q+); a mean-pool lane owns 4
+// channels of the key sum (paired with W sum_h q_h).
+template <int DT, int DESC, int D>
+struct ScoreGeom {
+    static constexpr int ES = (DESC == kMinMax) ? (DT == kBF16 ? 2 : 4) : 4;  // bytes/elem
+    static constexpr int EPL = 16 / ES;                                          // elems/lane
+    static constexpr int BR = (DESC == kMinMax ? 2 : 1) * D * ES;                // bytes/block
+    static constexpr int LPB = BR / 16;                                          // lanes/block
+    static constexpr int BPL = kWave / LPB;                // blocks per wave load
+    static constexpr int BPW = BPL * (kScoreThreads / kWave) * kScoreIters;  // blocks per WG
+};
+
 template <int DT, int DESC, int D>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
     typedef typename Elem<DT>::T E;
-    constexpr int DE = DESC == kMinMax ? DT : kF32;  // descriptor element type
-    constexpr int EPL = Chunk<DE>::N;                 // elements per lane
-    constexpr int LPB = D / EPL;                      // lanes per block row
-    constexpr int BPI = kScoreThreads / LPB;          // blocks per iteration
-    constexpr int BPW = BPI * kScoreIters;            // blocks per workgroup
+    typedef ScoreGeom<DT, DESC, D> Gm;
+    constexpr int EPL = Gm::EPL, LPB = Gm::LPB, BPL = Gm::BPL;
+    constexpr int DE = (Gm::ES == 2) ? kBF16 : kF32;
     const CacheArgs& c = p.c;
     const SelectArgs& a = p.s;
     const int grp = blockIdx.y;
     const int s = grp / c.Hkv;
     const int kvh = grp - s * c.Hkv;
+    const int c0 = blockIdx.x * Gm::BPW;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int lp = lane % LPB;   // lane position inside the block's bytes
+    const int bl = lane / LPB;   // which block of the wave load
+    // channels of this lane and which descriptor row it reads
+    const bool max_row = (DESC == kMinMax) && (lp * 16 >= D * Gm::ES);
+    const int ch0 = (lp * EPL) % D;
+
+    // 1. descriptor loads first, before anything they do not depend on is
+    //    known: indices are clamped to the descriptor array (max_blocks rows),
+    //    results past the candidates are discarded below, so every load of
+    //    the workgroup is in flight while the queries and the length arrive.
+    const char* base = static_cast<const char*>(c.desc) +
+                       (static_cast<int64_t>(grp) * c.max_blocks) * Gm::BR + lp * 16;
+    float x[kScoreIters][EPL];
+#pragma unroll
+    for (int it = 0; it < kScoreIters; ++it) {
+        const int j = min(c0 + (it * (kScoreThreads / kWave) + wave) * BPL + bl, c.max_blocks - 1);
+        Chunk<DE>::load(base + static_cast<int64_t>(j) * Gm::BR, x[it]);
+    }
+    // 2. the group's queries go through LDS in one parallel round trip
+    __shared__ float qs[16 * D];
+    const E* qg = static_cast<const E*>(a.q) + (static_cast<int64_t>(s) * c.Hq + kvh * c.G) * D;
+    for (int i = tid; i < c.G * D; i += kScoreThreads) qs[i] = Elem<DT>::load(qg, i);
     const int T = c.seq_lens[s];
     const int NB = (T + c.block - 1) / c.block;
     const int nl = min(a.n_local, NB);
     const int NC = NB - nl;
-    const int c0 = blockIdx.x * BPW;
-    if (c0 >= NC) return;
-    const int c1 = min(c0 + BPW, NC);
-    const int tid = threadIdx.x;
-    const int lp = tid % LPB;      // lane position inside the block row
-    const int slot = tid / LPB;    // which block of the iteration
-    const int ch0 = lp * EPL;      // first channel of this lane
-
-    const E* qg = static_cast<const E*>(a.q) + (static_cast<int64_t>(s) * c.Hq + kvh * c.G) * D;
-    float wa[EPL], wb[EPL];
+    __syncthreads();
+    if (c0 >= NC) return;  // uniform across the workgroup
+    float wv[EPL];
     if (DESC == kMinMax) {
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            float qp = 0.f, qm = 0.f;
+            float acc = 0.f;
             for (int h = 0; h < c.G; ++h) {
-                const float x = Elem<DT>::load(qg, h * D + ch0 + e);
-                qp += fmaxf(x, 0.f);
-                qm += fminf(x, 0.f);
+                const float xq = qs[h * D + ch0 + e];
+                acc += max_row ? fmaxf(xq, 0.f) : fminf(xq, 0.f);
             }
-            wa[e] = qp;  // pairs with the max row
-            wb[e] = qm;  // pairs with the min row
+            wv[e] = acc;
         }
     } else {
+        // u = sum_h q_h (once, in LDS), then w = W u for this lane's channels
         __shared__ float u_s[D];
         for (int i = tid; i < D; i += kScoreThreads) {
             float acc = 0.f;
-            for (int h = 0; h < c.G; ++h) acc += Elem<DT>::load(qg, h * D + i);
+            for (int h = 0; h < c.G; ++h) acc += qs[h * D + i];
             u_s[i] = acc;
         }
         __syncthreads();
@@ -119,39 +152,29 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
         for (int e = 0; e < EPL; ++e) {
             const uint16_t* wr = W + (ch0 + e) * D;
             float acc = 0.f;
+#pragma unroll 4
             for (int k = 0; k < D; ++k) acc += bf2f(wr[k]) * u_s[k];
-            wa[e] = acc;
-            wb[e] = 0.f;
+            wv[e] = acc;
         }
     }
 
-    float* out = a.scores + static_cast<int64_t>(grp) * c.max_blocks;
-    const int64_t row0 = static_cast<int64_t>(grp) * c.max_blocks;
-    for (int jb = c0; jb < c1; jb += BPI) {
-        const int j = jb + slot;
-        if (j >= c1) break;  // whole lane run leaves together
-        float part = 0.f;
-        if (DESC == kMinMax) {
-            const E* dp = static_cast<const E*>(c.desc) + (row0 + j) * 2 * D;
-            float mn[EPL], mx[EPL];
-            Chunk<DE>::load(dp + ch0, mn);
-            Chunk<DE>::load(dp + D + ch0, mx);
+    float part[kScoreIters];
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) part += wa[e] * mx[e] + wb[e] * mn[e];
-        } else {
-            const float* dp = static_cast<const float*>(c.desc) + (row0 + j) * D;
-            float sm[EPL];
-            Chunk<kF32>::load(dp + ch0, sm);
+    for (int it = 0; it < kScoreIters; ++it) {
+        float acc = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) part += wa[e] * sm[e];
-        }
-        part = group_sum<LPB>(part);
-        if (lp == 0) {
-            if (DESC == kMeanPool) {
-                const int ntok = min(c.block, T - j * c.block);
-                part = part / static_cast<float>(ntok);
-            }
-            out[j] = part;
+        for (int e = 0; e < EPL; ++e) acc += wv[e] * x[it][e];
+        part[it] = acc;
+    }
+    float* out = a.scores + static_cast<int64_t>(grp) * p.stride;
+#pragma unroll
+    for (int it = 0; it < kScoreIters; ++it) {
+        const float tot = group_sum<LPB>(part[it]);
+        const int j = c0 + (it * (kScoreThreads / kWave) + wave) * BPL + bl;
+        if (lp == 0 && j < NC) {
+            float v = tot;
+            if (DESC == kMeanPool) v = v / static_cast<float>(min(c.block, T - j * c.block));
+            out[j] = v;
         }
     }
 }
@@ -177,41 +200,29 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
     }
     return x;
 }
-// Exclusive prefix sum over all kTopnThreads threads; *total gets the sum.
-__device__ __forceinline__ int block_excl_scan(int v, int* wsum, int* total) {
-    const int w = threadIdx.x >> 6;
-    const int incl = wave_incl_scan(v);
-    if ((threadIdx.x & 63) == 63) wsum[w] = incl;
-    __syncthreads();
-    int before = 0, all = 0;
-#pragma unroll
-    for (int k = 0; k < kTopnWaves; ++k) {
-        const int t = wsum[k];
-        before += (k < w) ? t : 0;
-        all += t;
-    }
-    __syncthreads();
-    *total = all;
-    return before + incl - v;
-}
 
 struct TopnParams {
     CacheArgs c;
     SelectArgs s;
+    int stride;  // score row stride (floats), a multiple of 4
 };
 
 template <int KPT>
 __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     const CacheArgs& c = p.c;
     const SelectArgs& a = p.s;
-    __shared__ int hist[256];
+    // three rotating histograms: pass k counts into hist[k%3] and clears
+    // hist[(k+1)%3], which nobody reads any more (its pass ended two
+    // barriers ago), so every radix pass needs a single barrier
+    __shared__ int hist[3][256];
     __shared__ int wsum[kTopnWaves];
     __shared__ uint32_t red_min[kTopnWaves], red_max[kTopnWaves];
-    __shared__ int s_digit, s_above;
 
     const int grp = blockIdx.x;
     const int s = grp / c.Hkv;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
     const int T = c.seq_lens[s];
     const int NB = (T + c.block - 1) / c.block;
     const int nl = min(a.n_local, NB);
@@ -219,18 +230,30 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     const int n = block_count(NB, c.block, a.budget_tokens, a.sparsity_bp, a.n_local, a.n_min);
     const int K = n - nl;  // candidates to pick
     int32_t* out = a.idx + static_cast<int64_t>(grp) * a.n_max;
-    const float* sc = a.scores + static_cast<int64_t>(grp) * c.max_blocks;
+    const float* sc = a.scores + static_cast<int64_t>(grp) * p.stride;
 
     const int base = tid * KPT;
     uint32_t key[KPT];
+    if (KPT >= 4) {
+        // branch-free 16-byte loads: the row is padded to a multiple of 4 and
+        // groups past the end read the row's first group (results unused)
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-        const int j = base + r;
-        key[r] = (j < NC) ? float_key(sc[j]) : 0u;
+        for (int r = 0; r < KPT; r += 4) {
+            const int g0 = (base + r < NC) ? base + r : 0;
+            const floatx4 v = *reinterpret_cast<const floatx4*>(sc + g0);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) key[r + k] = float_key(v[k]);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) key[r] = float_key(sc[(base + r < NC) ? base + r : 0]);
     }
 
-    // mode: 0 = none, 1 = all candidates, 2 = threshold
-    int mode = (K <= 0) ? 0 : (K >= NC ? 1 : 2);
+    // mode: 0 = pick none, 1 = pick every candidate, 2 = threshold select
+    const int mode = (K <= 0) ? 0 : (K >= NC ? 1 : 2);
+    if (mode == 1) {
+        for (int j = tid; j < NC; j += kTopnThreads) out[j] = j;
+    }
     uint32_t tau = 0;
     int need_eq = 0;
     if (mode == 2) {
@@ -244,10 +267,11 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         }
         lmin = wave_min_u32(lmin);
         lmax = wave_max_u32(lmax);
-        if ((tid & 63) == 0) {
-            red_min[tid >> 6] = lmin;
-            red_max[tid >> 6] = lmax;
+        if (lane == 0) {
+            red_min[wave] = lmin;
+            red_max[wave] = lmax;
         }
+        if (tid < 256) hist[0][tid] = 0;
         __syncthreads();
         uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -256,95 +280,95 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             kmax = max(kmax, red_max[w]);
         }
         const uint32_t range = kmax - kmin;
-        uint32_t prefix = 0;  // over key - kmin
+        uint32_t prefix = 0;  // of key - kmin, above the current digit
         int krem = K;
         int shift = (range == 0u) ? 0 : 32 - __clz(static_cast<int>(range));
+        int pass = 0;
         while (shift > 0) {
             const int dbits = min(8, shift);
             shift -= dbits;
-            const int hi = shift + dbits;  // bits above the digit must match prefix
-            for (int b = tid; b < 256; b += kTopnThreads) hist[b] = 0;
-            __syncthreads();
+            const int hi = shift + dbits;
+            int* h = hist[pass % 3];
 #pragma unroll
             for (int r = 0; r < KPT; ++r) {
                 if (base + r < NC) {
                     const uint32_t kr = key[r] - kmin;
                     const bool alive = hi >= 32 || ((kr >> hi) == (prefix >> hi));
-                    if (alive) atomicAdd(&hist[(kr >> shift) & ((1u << dbits) - 1u)], 1);
+                    if (alive) atomicAdd(&h[(kr >> shift) & ((1u << dbits) - 1u)], 1);
                 }
             }
+            if (tid < 256) hist[(pass + 1) % 3][tid] = 0;
             __syncthreads();
-            // suffix counts over the digits: thread t < 256 looks at digit 255 - t
-            // (waves 0..3 are whole waves, so the in-wave scan is well formed)
-            int h = 0, incl = 0;
-            if (tid < 256) {
-                h = hist[255 - tid];
-                incl = wave_incl_scan(h);
-                if ((tid & 63) == 63) wsum[tid >> 6] = incl;
+            // every wave finds the digit on its own: lane L covers digits
+            // 255-4L .. 252-4L (descending), counts are suffix sums
+            int c4[4], hv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hv[i] = h[255 - 4 * lane - i];
+            c4[0] = hv[0];
+#pragma unroll
+            for (int i = 1; i < 4; ++i) c4[i] = c4[i - 1] + hv[i];
+            const int incl = wave_incl_scan(c4[3]);
+            const int excl = incl - c4[3];
+            int found_i = -1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ge = excl + c4[i];  // keys whose digit >= this one
+                if (ge >= krem && ge - hv[i] < krem) found_i = i;
             }
-            __syncthreads();
-            if (tid < 256) {
-                int before = 0;
-                for (int w = 0; w < (tid >> 6); ++w) before += wsum[w];
-                const int ge = before + incl;  // keys whose digit >= 255 - tid
-                if (ge >= krem && ge - h < krem) {  // exactly one thread
-                    s_digit = 255 - tid;
-                    s_above = ge - h;
-                }
-            }
-            __syncthreads();
-            prefix |= static_cast<uint32_t>(s_digit) << shift;
-            krem -= s_above;
-            __syncthreads();
+            const uint64_t bal = __ballot(found_i >= 0);
+            const int src = __ffsll(static_cast<unsigned long long>(bal)) - 1;  // exactly one lane
+            const int my_digit = 255 - 4 * lane - (found_i < 0 ? 0 : found_i);
+            const int my_above = excl + (found_i <= 0 ? 0 : c4[found_i - 1]);
+            const int digit = __shfl(my_digit, src, 64);
+            const int above = __shfl(my_above, src, 64);
+            prefix |= static_cast<uint32_t>(digit) << shift;
+            krem -= above;
+            ++pass;
         }
         tau = kmin + prefix;
         need_eq = krem;
-    }
 
-    // compaction in ascending index order
-    int total = 0;
-    int n_eq = 0;
-    if (mode == 2) {
+        // one packed scan: (keys > tau) << 16 | (keys == tau), per thread
+        int n_gt = 0, n_eq = 0;
 #pragma unroll
-        for (int r = 0; r < KPT; ++r) n_eq += (base + r < NC && key[r] == tau) ? 1 : 0;
-    }
-    int eq_rank = block_excl_scan(n_eq, wsum, &total);
-    bool sel[KPT];
-    int n_sel = 0;
+        for (int r = 0; r < KPT; ++r) {
+            const bool valid = base + r < NC;
+            n_gt += (valid && key[r] > tau) ? 1 : 0;
+            n_eq += (valid && key[r] == tau) ? 1 : 0;
+        }
+        const int packed = (n_gt << 16) | n_eq;
+        const int incl = wave_incl_scan(packed);
+        if (lane == 63) wsum[wave] = incl;
+        __syncthreads();
+        int before = 0;
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-        const bool valid = base + r < NC;
-        bool take;
-        if (mode == 0)
-            take = false;
-        else if (mode == 1)
-            take = valid;
-        else if (valid && key[r] > tau)
-            take = true;
-        else if (valid && key[r] == tau) {
-            take = eq_rank < need_eq;
-            ++eq_rank;
-        } else
-            take = false;
-        sel[r] = take;
-        n_sel += take ? 1 : 0;
-    }
-    int pos = block_excl_scan(n_sel, wsum, &total);
+        for (int w = 0; w < kTopnWaves; ++w) before += (w < wave) ? wsum[w] : 0;
+        const int excl = before + incl - packed;
+        int eq_rank = excl & 0xffff;
+        int pos = (excl >> 16) + min(eq_rank, need_eq);
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-        if (sel[r]) out[pos++] = base + r;
+        for (int r = 0; r < KPT; ++r) {
+            const bool valid = base + r < NC;
+            bool take = false;
+            if (valid && key[r] > tau) {
+                take = true;
+            } else if (valid && key[r] == tau) {
+                take = eq_rank < need_eq;
+                ++eq_rank;
+            }
+            if (take) out[pos++] = base + r;
+        }
     }
+    const int picked = (mode == 0) ? 0 : K;
     // local blocks follow the picked candidates (their ids are the largest)
-    for (int t = tid; t < nl; t += kTopnThreads) out[total + t] = NC + t;
-    for (int t = total + nl + tid; t < a.n_max; t += kTopnThreads) out[t] = -1;
-    if (tid == 0) a.cnt[grp] = total + nl;
+    for (int t = tid; t < nl; t += kTopnThreads) out[picked + t] = NC + t;
+    for (int t = picked + nl + tid; t < a.n_max; t += kTopnThreads) out[t] = -1;
+    if (tid == 0) a.cnt[grp] = picked + nl;
 }
 
 template <int DT, int DESC, int D>
 hipError_t launch_score(const ScoreParams& p, hipStream_t stream) {
-    constexpr int DE = DESC == kMinMax ? DT : kF32;
-    constexpr int EPL = DE == kBF16 ? 8 : 4;
-    constexpr int BPW = (kScoreThreads / (D / EPL)) * kScoreIters;
+    constexpr int BPW = ScoreGeom<DT, DESC, D>::BPW;
     dim3 grid((p.c.max_blocks + BPW - 1) / BPW, p.c.B * p.c.Hkv);
     hipLaunchKernelGGL((score_kernel<DT, DESC, D>), grid, dim3(kScoreThreads), 0, stream, p);
     return hipGetLastError();
@@ -357,11 +381,14 @@ hipError_t launch_score_d(const ScoreParams& p, hipStream_t stream) {
 
 template <int KPT>
 hipError_t launch_topn_k(const TopnParams& p, hipStream_t stream) {
+    static_assert(KPT >= 4 || KPT == 1 || KPT == 2, "keys per thread");
     hipLaunchKernelGGL((topn_kernel<KPT>), dim3(p.c.B * p.c.Hkv), dim3(kTopnThreads), 0, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
+
+int score_stride(int max_blocks) { return (max_blocks + 3) & ~3; }
 
 int topn_keys_per_thread(int max_blocks) {
     for (int k = 1; k <= 32; k <<= 1)
@@ -370,7 +397,7 @@ int topn_keys_per_thread(int max_blocks) {
 }
 
 hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t stream) {
-    ScoreParams sp{c, s};
+    ScoreParams sp{c, s, score_stride(c.max_blocks)};
     hipError_t err;
     if (c.dtype == kBF16)
         err = c.desc_kind == kMinMax ? launch_score_d<kBF16, kMinMax>(sp, stream)
@@ -379,7 +406,7 @@ hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t st
         err = c.desc_kind == kMinMax ? launch_score_d<kF32, kMinMax>(sp, stream)
                                      : launch_score_d<kF32, kMeanPool>(sp, stream);
     if (err != hipSuccess) return err;
-    TopnParams tp{c, s};
+    TopnParams tp{c, s, score_stride(c.max_blocks)};
     switch (topn_keys_per_thread(c.max_blocks)) {
         case 1: return launch_topn_k<1>(tp, stream);
         case 2: return launch_topn_k<2>(tp, stream);
