@@ -34,6 +34,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kChunkTiles = 64;  // 2048 tokens per workgroup
+constexpr int kStages = 4;       // tiles in flight per workgroup (LDS ring)
 
 struct RectifyParams {
     CacheArgs c;
@@ -51,14 +52,39 @@ __device__ __forceinline__ void store_empty(float* o_part, float* lse_part, int6
     if (ch == 0) lse_part[row * S + split] = -INFINITY;
 }
 
-template <int D, int BLK, int RTW>
-__global__ __launch_bounds__(kThreads) void rectify_bf16_kernel(RectifyParams p) {
+// Direct copy of 16 bytes per lane from global memory into LDS: lane L's
+// bytes land at lds + 16 L (lds is wave-uniform; it goes into M0).  Written
+// in asm so that the compiler does not treat it as an LDS write it must
+// drain before every LDS read; the kernels order it themselves with explicit
+// vector-memory waits and barriers.  The instruction has no register output.
+__device__ __forceinline__ void copy16_to_lds(const void* src, void* lds) {
+    // the low 32 bits of a generic LDS address are the LDS offset
+    const uint32_t m0 =
+        __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src));
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int D, int BLK, int RTW, int NS, int NW>
+__global__ __launch_bounds__(NW * kWave) void rectify_bf16_kernel(RectifyParams p) {
     constexpr int KS = D / 32;
     constexpr int NT = D / 16;
-    constexpr int TILE_EL = 32 * D;          // elements of K (or V) per tile
-    constexpr int CHUNKS = TILE_EL / 8;      // 16-byte pieces per tile
-    constexpr int PER_T = CHUNKS / kThreads; // pieces per thread (K or V)
-    __shared__ __attribute__((aligned(16))) uint16_t stage[2][2 * TILE_EL];
+    constexpr int TILE_EL = 32 * D;             // elements of K (or V) per tile
+    constexpr int CH = 2 * TILE_EL / 512;       // 1 KiB chunks per tile, K then V
+    constexpr int CPW = CH / NW;                // chunks each wave copies
+    static_assert(CPW >= 1 && CPW * NW == CH, "chunks split evenly over the waves");
+    // NS-stage ring of tiles in LDS, filled by direct global->LDS copies
+    // (copy16_to_lds): each wave copies CPW KiB chunks per tile, NS-1 tiles
+    // ahead of the one being computed, without using registers.
+    __shared__ __attribute__((aligned(16))) uint16_t ring[NS][2 * TILE_EL];
+    __shared__ int s_page[kChunkTiles * 32 / 32 + 2];
 
     const CacheArgs& c = p.c;
     const RectifyArgs& a = p.a;
@@ -76,12 +102,19 @@ __global__ __launch_bounds__(kThreads) void rectify_bf16_kernel(RectifyParams p)
     const int g = lane >> 4;
     const int col = lane & 15;
     const int64_t row_base = (static_cast<int64_t>(s) * c.Hq + kvh * G) * f;  // output row of r = 0
-    const int rt0 = (blockIdx.z * kWaves + wave) * RTW;  // first 16-row tile of this wave
+    const int rt0 = (blockIdx.z * NW + wave) * RTW;  // first 16-row tile of this wave
 
     const int ntiles = (T + 31) / 32;
     const int t0 = split * a.chunk_tiles;
     const int t1 = min(t0 + a.chunk_tiles, ntiles);
     if (t0 >= t1) return;  // the merge only reads the chunks that cover [0, T)
+    const int nt = t1 - t0;
+
+    // page ids of the chunk's blocks (tiles are 32 tokens, blocks BLK tokens)
+    const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
+    const int blk0 = (32 * t0) / BLK;
+    const int nblk = (32 * (t1 - 1)) / BLK - blk0 + 1;
+    for (int i = threadIdx.x; i < nblk; i += NW * kWave) s_page[i] = ptrow[blk0 + i];
 
     // B operand of S^T = K Q^T for each row tile: row rt*16 + col
     bf16x8 qb[RTW][KS];
@@ -110,42 +143,51 @@ __global__ __launch_bounds__(kThreads) void rectify_bf16_kernel(RectifyParams p)
 
     const uint16_t* kpool = static_cast<const uint16_t*>(c.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(c.v_pool);
-    const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
     const float sl2 = a.scale_log2;
+    // retire the query and page-table loads before the copy ring starts, so
+    // that no wait for them lands inside the loop (where it would also drain
+    // the copies in flight)
+    wait_vmcnt<0>();
+    __syncthreads();  // s_page
 
-    u32x4 pre_k[PER_T], pre_v[PER_T];
-    auto fetch = [&](int t) {
+    // queue the copies of tile t into ring stage buf
+    auto issue = [&](int t, int buf) __attribute__((always_inline)) {
         const int tok0 = 32 * t;
         const int blk = tok0 / BLK;
-        const int64_t page = ptrow[blk];
-        const int64_t off = (page * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) + (tok0 - blk * BLK) * D;
+        const int page = __builtin_amdgcn_readfirstlane(s_page[blk - blk0]);
+        const int64_t off = (static_cast<int64_t>(page) * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) +
+                            (tok0 - blk * BLK) * D + lane * 8;
 #pragma unroll
-        for (int k = 0; k < PER_T; ++k) {
-            const int piece = threadIdx.x + k * kThreads;
-            pre_k[k] = ldg16(kpool + off + piece * 8);
-            pre_v[k] = ldg16(vpool + off + piece * 8);
-        }
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-        for (int k = 0; k < PER_T; ++k) {
-            const int piece = threadIdx.x + k * kThreads;
-            *reinterpret_cast<u32x4*>(&stage[buf][piece * 8]) = pre_k[k];
-            *reinterpret_cast<u32x4*>(&stage[buf][TILE_EL + piece * 8]) = pre_v[k];
+        for (int i = 0; i < CPW; ++i) {
+            const int ch = wave * CPW + i;
+            const uint16_t* src = (ch < CH / 2) ? kpool + off + ch * 512
+                                                : vpool + off + (ch - CH / 2) * 512;
+            copy16_to_lds(src, &ring[buf][ch * 512]);
         }
     };
 
-    fetch(t0);
-    stash(0);
-    __syncthreads();
-    for (int t = t0; t < t1; ++t) {
-        const int buf = (t - t0) & 1;
-        if (t + 1 < t1) fetch(t + 1);
-        const uint16_t* ks_lds = &stage[buf][lane * 8];
-        const uint16_t* vs_lds = &stage[buf][TILE_EL + lane * 8];
+#pragma unroll
+    for (int k = 0; k < NS - 1; ++k)
+        if (k < nt) issue(t0 + k, k);
+    for (int k = 0; k < nt; ++k) {
+        const int t = t0 + k;
+        const uint16_t* st = ring[k % NS];
+        // every wave is done reading the stage refilled next (it held tile k-1)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (k + NS - 1 < nt) {
+            issue(t + NS - 1, (k + NS - 1) % NS);
+            wait_vmcnt<CPW * (NS - 1)>();  // this wave's copies of tile k have landed
+        } else {
+            wait_vmcnt<0>();
+        }
+        __builtin_amdgcn_s_barrier();  // ... and every other wave's
+        asm volatile("" ::: "memory");  // no LDS read moves above this point
+    const uint16_t* ks_lds = st + lane * 8;
+        const uint16_t* vs_lds = st + TILE_EL + lane * 8;
         u32x4 kr[2 * KS];
 #pragma unroll
-        for (int k = 0; k < 2 * KS; ++k) kr[k] = *reinterpret_cast<const u32x4*>(ks_lds + k * 512);
+        for (int kk = 0; kk < 2 * KS; ++kk) kr[kk] = *reinterpret_cast<const u32x4*>(ks_lds + kk * 512);
         u32x4 vr[NT];
 #pragma unroll
         for (int n = 0; n < NT; ++n) vr[n] = *reinterpret_cast<const u32x4*>(vs_lds + n * 512);
@@ -153,12 +195,12 @@ __global__ __launch_bounds__(kThreads) void rectify_bf16_kernel(RectifyParams p)
         const int nvalid = T - tok0;  // >= 1
         if (nvalid < 32) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int tok = (k < 4) ? (4 * g + k) : (16 + 4 * g + k - 4);
+            for (int kk = 0; kk < 8; ++kk) {
+                const int tok = (kk < 4) ? (4 * g + kk) : (16 + 4 * g + kk - 4);
                 if (tok >= nvalid) {
-                    const uint32_t keep = (k & 1) ? 0x0000ffffu : 0xffff0000u;
+                    const uint32_t keep = (kk & 1) ? 0x0000ffffu : 0xffff0000u;
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) vr[n][k >> 1] &= keep;
+                    for (int n = 0; n < NT; ++n) vr[n][kk >> 1] &= keep;
                 }
             }
         }
@@ -174,55 +216,50 @@ __global__ __launch_bounds__(kThreads) void rectify_bf16_kernel(RectifyParams p)
                         __builtin_bit_cast(bf16x8, kr[mt * KS + ks]), qb[rt][ks], sacc[mt], 0, 0, 0);
             }
             float x[8];
-            float tmax = -INFINITY;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int tok = tok0 + ((k < 4) ? (4 * g + k) : (16 + 4 * g + k - 4));
-                const float v = sacc[k >> 2][k & 3] * sl2;
-                x[k] = (tok <= pos[rt]) ? v : -INFINITY;
-                tmax = fmaxf(tmax, x[k]);
+            for (int kk = 0; kk < 8; ++kk) x[kk] = sacc[kk >> 2][kk & 3] * sl2;
+            if (tok0 + 31 > T - f) {  // the causal mask only bites in the last f tokens
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const int tok = tok0 + ((kk < 4) ? (4 * g + kk) : (16 + 4 * g + kk - 4));
+                    x[kk] = (tok <= pos[rt]) ? x[kk] : -INFINITY;
+                }
             }
+            float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                               fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            const float m_new = fmaxf(m_run[rt], tmax);
-            const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // row sees nothing yet
-            const float alpha = exp2f(m_run[rt] - m_use);
+            if (__ballot(tmax > m_run[rt]) != 0) {  // some row's running max grows
+                const float m_new = fmaxf(m_run[rt], tmax);
+                const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
+                l_run[rt] *= alpha;
+                m_run[rt] = m_new;
+                float al[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * g + e, 64);
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) oacc[rt][n][e] *= al[e];
+            }
+            const float m_use = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];  // row sees nothing yet
             float pr[8];
-            float psum = 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                pr[k] = exp2f(x[k] - m_use);
-                psum += pr[k];
-            }
-            l_run[rt] = l_run[rt] * alpha + psum;
-            m_run[rt] = m_new;
-            float al[4];
+            for (int kk = 0; kk < 8; ++kk) pr[kk] = __builtin_amdgcn_exp2f(x[kk] - m_use);
+            l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+            bf16x8 ph, pl;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * g + e, 64);
+            for (int kk = 0; kk < 8; ++kk) ph[kk] = static_cast<__bf16>(pr[kk]);
 #pragma unroll
-            for (int n = 0; n < NT; ++n)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) oacc[rt][n][e] *= al[e];
-            u32x4 phi, plo;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint16_t h0 = f2bf(pr[2 * k]);
-                const uint16_t h1 = f2bf(pr[2 * k + 1]);
-                phi[k] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-                plo[k] = pack_bf2(pr[2 * k] - bf2f(h0), pr[2 * k + 1] - bf2f(h1));
-            }
-            const bf16x8 ph = __builtin_bit_cast(bf16x8, phi);
-            const bf16x8 pl = __builtin_bit_cast(bf16x8, plo);
+            for (int kk = 0; kk < 8; ++kk)
+                pl[kk] = static_cast<__bf16>(pr[kk] - static_cast<float>(ph[kk]));
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
                 const bf16x8 vb = __builtin_bit_cast(bf16x8, vr[n]);
                 oacc[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, oacc[rt][n], 0, 0, 0);
                 oacc[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[rt][n], 0, 0, 0);
             }
-        }
-        if (t + 1 < t1) stash(buf ^ 1);
-        __syncthreads();
-    }
+        }    }
 
     // partials for this wave's rows
 #pragma unroll
@@ -315,21 +352,25 @@ __global__ __launch_bounds__(kThreads) void rectify_f32_kernel(RectifyParams p) 
     }
 }
 
-template <int D, int BLK, int RTW>
+template <int D, int BLK, int RTW, int NW>
 hipError_t launch_bf16(const RectifyParams& p, hipStream_t stream) {
     const int R = p.c.G * p.a.f;
-    const int rows_per_wg = 64 * RTW;
+    const int rows_per_wg = 16 * RTW * NW;
     dim3 grid(p.a.splits, p.c.B * p.c.Hkv, (R + rows_per_wg - 1) / rows_per_wg);
-    hipLaunchKernelGGL((rectify_bf16_kernel<D, BLK, RTW>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((rectify_bf16_kernel<D, BLK, RTW, kStages, NW>), grid, dim3(NW * kWave), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
+// Rows (G*f) per workgroup: up to 64 with 4 waves, up to 128 with 8 waves of
+// one 16-row tile each (two waves per SIMD), 256 with 8 waves of two tiles;
+// more rows take several workgroups along z.
 template <int D, int BLK>
 hipError_t launch_bf16_r(const RectifyParams& p, hipStream_t stream) {
     const int R = p.c.G * p.a.f;
-    if (R <= 64) return launch_bf16<D, BLK, 1>(p, stream);
-    if (R <= 128) return launch_bf16<D, BLK, 2>(p, stream);
-    return launch_bf16<D, BLK, 4>(p, stream);
+    if (R <= 64) return launch_bf16<D, BLK, 1, 4>(p, stream);
+    if (R <= 128) return launch_bf16<D, BLK, 1, 8>(p, stream);
+    return launch_bf16<D, BLK, 2, 8>(p, stream);
 }
 
 template <int D>
