@@ -76,15 +76,14 @@ DecodeWs decode_ws(const CacheArgs& c, int n_max) {
 
 struct RectifyWs {
     size_t o_part, lse_part, total;
-    int splits, chunk_tiles;
+    RectifyPlan plan;
 };
 RectifyWs rectify_ws(const CacheArgs& c, int f) {
     RectifyWs w;
-    rectify_splits(c, f, &w.splits, &w.chunk_tiles);
-    const size_t rows = static_cast<size_t>(c.B) * c.Hq * f;
+    rectify_plan(c, f, &w.plan);
     w.o_part = 0;
-    w.lse_part = align_up(rows * w.splits * c.d * sizeof(float));
-    w.total = w.lse_part + align_up(rows * w.splits * sizeof(float));
+    w.lse_part = align_up(static_cast<size_t>(w.plan.o_floats) * sizeof(float));
+    w.total = w.lse_part + align_up(static_cast<size_t>(w.plan.lse_floats) * sizeof(float));
     return w;
 }
 
@@ -235,8 +234,10 @@ bsa_status bsa_rectify_chunk(const bsa_layout* layout, const bsa_cache* cache, c
     a.k_new = k_new;
     a.v_new = v_new;
     a.f = f;
-    a.splits = w.splits;
-    a.chunk_tiles = w.chunk_tiles;
+    a.splits = w.plan.splits;
+    a.chunk_tiles = w.plan.chunk_tiles;
+    a.wgs = w.plan.wgs;
+    a.rows_per_wg = w.plan.rows_per_wg;
     a.scale_log2 = softmax_scale * kLog2e;
     a.o_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.o_part);
     a.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.lse_part);

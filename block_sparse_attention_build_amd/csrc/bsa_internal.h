@@ -60,16 +60,26 @@ struct RectifyArgs {
     const void* k_new;  // [B][Hkv][f][d]
     const void* v_new;
     int f;
-    int splits;           // token chunks per group
-    int chunk_tiles;      // 32-token tiles per chunk
+    int splits;           // fp32: token chunks per group
+    int chunk_tiles;      // fp32: 32-token tiles per chunk
+    int wgs;              // bf16: workgroups launched (even shares of all tiles)
+    int rows_per_wg;      // bf16: rows of a row group
     float scale_log2;
-    float* o_part;        // [B*Hq*f][S][d]
-    float* lse_part;      // [B*Hq*f][S]
+    float* o_part;        // bf16: [slot][rows_per_wg][d]; fp32: [B*Hq*f][S][d]
+    float* lse_part;      // bf16: [slot][rows_per_wg];    fp32: [B*Hq*f][S]
     void* o;
     float* lse;
 };
+// Sizes of the partial results of one rectify call (floats) and the launch
+// shape they follow.
+struct RectifyPlan {
+    int64_t o_floats;
+    int64_t lse_floats;
+    int splits, chunk_tiles;  // fp32 path
+    int wgs, rows_per_wg;     // bf16 path
+};
 hipError_t launch_rectify(const CacheArgs& c, const RectifyArgs& a, hipStream_t stream);
-void rectify_splits(const CacheArgs& c, int f, int* splits, int* chunk_tiles);
+void rectify_plan(const CacheArgs& c, int f, RectifyPlan* plan);
 
 // Merge S partials of `rows` rows into o (KV dtype) and lse (natural log).
 hipError_t launch_combine(int dtype, int d, int rows, int splits, const float* o_part,

@@ -12,8 +12,8 @@
 // matrix-operand order), then one thread per channel walks the block's
 // tokens in order to update or rebuild that channel's descriptor.  New-token
 // values are read from the source, older ones from the cache, so there is no
-// read-after-write hazard inside the workgroup.  Work per step is a few KiB;
-// this kernel is not on the bandwidth-critical path.
+// read-after-write hazard inside the workgroup.  Work per step is a few KiB,
+// so the kernel is latency-bound: every thread keeps kBatch loads in flight.
 #include "bsa_device.h"
 #include "bsa_internal.h"
 
@@ -22,6 +22,7 @@ namespace bsa {
 namespace {
 
 constexpr int kThreads = 128;
+constexpr int kBatch = 8;  // loads in flight per thread
 
 struct KvWriteParams {
     CacheArgs c;
@@ -64,57 +65,83 @@ __global__ __launch_bounds__(kThreads) void kv_write_kernel(KvWriteParams p) {
                          : nullptr;
 
     if (writes) {
+        // copy: kBatch independent source loads per thread before the stores
+        // (the stores could alias the sources as far as the compiler knows,
+        // so without the batching every load would wait for the last store)
         const int w0 = max(tb0, lo);
         const int nel = (tb1 - w0) * d;
         const E* ksrc = ks + static_cast<int64_t>(w0 - lo) * d;
         const E* vsrc = vs + static_cast<int64_t>(w0 - lo) * d;
-        for (int e = threadIdx.x; e < nel; e += kThreads) {
-            const int tt = e / d;
-            const int i = e - tt * d;
-            const int t = w0 - tb0 + tt;
-            kp[k_off<DT>(t, i, d)] = ksrc[e];
-            vp[v_off<DT>(t, i, d)] = vsrc[e];
+        for (int e0 = threadIdx.x; e0 < nel; e0 += kBatch * kThreads) {
+            E kb[kBatch], vb[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int e = e0 + u * kThreads;
+                if (e < nel) {
+                    kb[u] = ksrc[e];
+                    vb[u] = vsrc[e];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int e = e0 + u * kThreads;
+                if (e < nel) {
+                    const int tt = e / d;
+                    const int i = e - tt * d;
+                    const int t = w0 - tb0 + tt;
+                    kp[k_off<DT>(t, i, d)] = kb[u];
+                    vp[v_off<DT>(t, i, d)] = vb[u];
+                }
+            }
         }
     }
 
-    // descriptor of block j, one thread per channel
+    // descriptor of block j, one thread per channel; the block's keys are
+    // read kBatch tokens at a time (independent loads), then folded in token
+    // order
     const bool merge = (p.mode == kModeAppend) && (tb0 < lo);
     const int t_first = merge ? lo : tb0;
     const int64_t drow = static_cast<int64_t>(grp) * c.max_blocks + j;
     for (int i = threadIdx.x; i < d; i += kThreads) {
-        if (DESC == kMinMax) {
-            E* dp = static_cast<E*>(c.desc) + drow * 2 * d;
-            float mn = 0.f, mx = 0.f;
-            bool have = merge;
-            if (merge) {
+        float mn = 0.f, mx = 0.f, acc = 0.f;
+        bool have = merge;
+        if (merge) {
+            if (DESC == kMinMax) {
+                const E* dp = static_cast<const E*>(c.desc) + drow * 2 * d;
                 mn = Elem<DT>::load(dp, i);
                 mx = Elem<DT>::load(dp, d + i);
+            } else {
+                acc = static_cast<const float*>(c.desc)[drow * d + i];
             }
-            for (int t = t_first; t < tb1; ++t) {
-                const float v = (writes && t >= lo)
-                                    ? Elem<DT>::load(ks, static_cast<int64_t>(t - lo) * d + i)
-                                    : Elem<DT>::load(kp, k_off<DT>(t - tb0, i, d));
-                if (!have) {
-                    mn = v;
-                    mx = v;
+        }
+        for (int t0 = t_first; t0 < tb1; t0 += kBatch) {
+            float v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int t = t0 + u;
+                v[u] = 0.f;
+                if (t < tb1)
+                    v[u] = (writes && t >= lo) ? Elem<DT>::load(ks, static_cast<int64_t>(t - lo) * d + i)
+                                               : Elem<DT>::load(kp, k_off<DT>(t - tb0, i, d));
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                if (t0 + u >= tb1) break;
+                if (DESC == kMinMax) {
+                    mn = (!have || v[u] < mn) ? v[u] : mn;
+                    mx = (!have || v[u] > mx) ? v[u] : mx;
                     have = true;
                 } else {
-                    mn = v < mn ? v : mn;
-                    mx = v > mx ? v : mx;
+                    acc += v[u];
                 }
             }
+        }
+        if (DESC == kMinMax) {
+            E* dp = static_cast<E*>(c.desc) + drow * 2 * d;
             Elem<DT>::store(dp, i, mn);  // exact: mn/mx are stored values
             Elem<DT>::store(dp, d + i, mx);
         } else {
-            float* dp = static_cast<float*>(c.desc) + drow * d;
-            float acc = merge ? dp[i] : 0.0f;
-            for (int t = t_first; t < tb1; ++t) {
-                const float v = (writes && t >= lo)
-                                    ? Elem<DT>::load(ks, static_cast<int64_t>(t - lo) * d + i)
-                                    : Elem<DT>::load(kp, k_off<DT>(t - tb0, i, d));
-                acc += v;
-            }
-            dp[i] = acc;
+            static_cast<float*>(c.desc)[drow * d + i] = acc;
         }
     }
 }

@@ -10,19 +10,24 @@
 //
 // bf16 path: the only dense contraction of the method, on
 // v_mfma_f32_16x16x32_bf16.  Rows = the G*f queries of a GQA group (G*f = 128
-// for G = 4, f = 32).  One workgroup = (sequence, KV head, chunk of 32-token
-// tiles, group of up to 64*RTW rows); each of its 4 waves owns RTW 16-row
-// tiles.  K/V tiles (16 KiB at d = 128) are copied once per workgroup from HBM
-// into a double-buffered LDS stage with coalesced 16-byte loads (the next
-// tile's loads are in flight while the current one is computed) and every
-// wave reads its matrix operands from LDS with conflict-free 16-byte reads.
-// Per tile and 16-row tile: S^T = K Q^T (2 x d/32 MFMAs), causal mask, online
-// softmax, O += P V with P split into bf16 hi + lo (2 x d/16 x 2 MFMAs).
-// Each wave writes normalised partials (o, base-2 lse) for its own rows; the
-// log-sum-exp merge (decode.hip) combines the chunks.
+// for G = 4, f = 32), handled in row groups of up to 64 (4 waves), 128 (8
+// waves) or 256 (8 waves of two 16-row tiles) rows.  The tiles of all
+// (sequence, KV head, row group) groups are dealt out in equal contiguous
+// shares to a fixed number of workgroups (two per CU), so ragged lengths
+// cost no load imbalance; each run of a share inside one group yields one
+// partial (o, base-2 lse) per row, merged afterwards in list order.
+// K/V tiles (16 KiB at d = 128) stream through a 4-stage LDS ring fed by
+// direct global->LDS copies, three tiles ahead of the one being computed;
+// every wave reads its matrix operands from LDS with conflict-free 16-byte
+// reads.  Per tile and 16-row tile: S^T = K Q^T (2 x d/32 MFMAs), causal
+// mask, online softmax with a lazily moved reference max, O += P V with P in
+// bf16 (d/16 MFMAs).
 //
-// fp32 path: same chunking, plain VALU arithmetic.
+// fp32 path: fixed token chunks per workgroup, plain VALU arithmetic, the
+// chunk merge of decode.hip.
 #include <math.h>
+
+#include <algorithm>
 
 #include "bsa_device.h"
 #include "bsa_internal.h"
@@ -33,8 +38,18 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kChunkTiles = 64;  // 2048 tokens per workgroup
-constexpr int kStages = 4;       // tiles in flight per workgroup (LDS ring)
+#ifndef BSA_RECTIFY_CHUNK_TILES
+#define BSA_RECTIFY_CHUNK_TILES 64
+#endif
+#ifndef BSA_RECTIFY_STAGES
+#define BSA_RECTIFY_STAGES 4
+#endif
+#ifndef BSA_RECTIFY_WAVES_PER_EU
+#define BSA_RECTIFY_WAVES_PER_EU 4
+#endif
+constexpr float kRebase = 8.f;  // log2 headroom before the running max is moved
+constexpr int kChunkTiles = BSA_RECTIFY_CHUNK_TILES;  // 32-token tiles per workgroup
+constexpr int kStages = BSA_RECTIFY_STAGES;           // tiles in flight per workgroup (LDS ring)
 
 struct RectifyParams {
     CacheArgs c;
@@ -43,13 +58,6 @@ struct RectifyParams {
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
-}
-
-// Partials of rows that see no token of this chunk.
-__device__ __forceinline__ void store_empty(float* o_part, float* lse_part, int64_t row, int S,
-                                            int split, int D, int ch) {
-    o_part[(row * S + split) * D + ch] = 0.f;
-    if (ch == 0) lse_part[row * S + split] = -INFINITY;
 }
 
 // Direct copy of 16 bytes per lane from global memory into LDS: lane L's
@@ -72,215 +80,443 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// ---------------------------------------------------------------------------
+// Work split of the bf16 path (stream-K style).  The attention of one call is
+// a set of groups (sequence, KV head, row group) in that order, group g
+// holding the ceil(T/32) tiles of its sequence; the groups' tiles, laid end
+// to end, form one list of N tiles.  Workgroup w of W takes the tiles
+// [w N / W, (w+1) N / W), whatever groups they belong to, so every workgroup
+// gets the same work however ragged the lengths are.  Each maximal run of a
+// workgroup's tiles inside one group (a "piece") yields one partial (o, lse)
+// per row, stored in slot g + w: along the list, every new piece moves to
+// the next group, the next workgroup or both, so g + w grows strictly and
+// slots never collide; there are fewer than (groups + W).
+// ---------------------------------------------------------------------------
+constexpr int kStreamWGs = 512;       // two workgroups per CU on a 256-CU part
+constexpr int kMinTilesPerWG = 16;    // fewer workgroups for small calls
+constexpr int kMaxTilesPerWG = 256;   // bounds the per-piece page list
+
+__device__ __forceinline__ int ntiles_of(int T) { return (T + 31) / 32; }
+
+// Workgroups used for N tiles when `launched` were launched (launched is at
+// least ceil(N_max / kMaxTilesPerWG) for the cache's capacity N_max).
+__device__ __forceinline__ int stream_wgs(int64_t N, int launched) {
+    if (N <= 0) return 0;
+    const int64_t lo = (N + kMaxTilesPerWG - 1) / kMaxTilesPerWG;
+    const int64_t hi = min(static_cast<int64_t>(kStreamWGs), (N + kMinTilesPerWG - 1) / kMinTilesPerWG);
+    return static_cast<int>(min(max(lo, hi), static_cast<int64_t>(launched)));
+}
+__device__ __forceinline__ int64_t wg_begin(int w, int64_t N, int W) {
+    return static_cast<int64_t>(w) * N / W;
+}
+// the workgroup whose range holds tile x: the largest w with wg_begin(w) <= x
+__device__ __forceinline__ int wg_owner(int64_t x, int64_t N, int W) {
+    return static_cast<int>(((x + 1) * W + N - 1) / N - 1);
+}
+
+// Wave-wide scan over the sequences: total tiles N of all groups, and (when
+// x >= 0) the sequence holding list position x with the list position of its
+// first tile.  per_seq = groups per sequence (Hkv * row groups).  Every lane
+// returns the same values.
+struct SeqHit {
+    int64_t N;
+    int s;           // -1 if x is not in the list
+    int64_t start;   // list position of sequence s's first tile
+};
+__device__ __forceinline__ SeqHit seq_scan(const int32_t* seq_lens, int B, int per_seq, int64_t x) {
+    const int lane = threadIdx.x & 63;
+    SeqHit h{0, -1, 0};
+    for (int s0 = 0; s0 < B; s0 += kWave) {
+        const int sq = s0 + lane;
+        const long long per = (sq < B) ? static_cast<long long>(ntiles_of(seq_lens[sq])) * per_seq : 0;
+        long long incl = per;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const long long y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        const int64_t excl = h.N + incl - per;
+        const uint64_t m = __ballot(h.s < 0 && x >= excl && x < h.N + incl);
+        if (m != 0) {
+            const int L = __builtin_ctzll(m);
+            h.s = s0 + L;
+            h.start = __shfl(static_cast<long long>(excl), L, 64);
+        }
+        h.N += __shfl(incl, 63, 64);
+    }
+    return h;
+}
+
+// Eight waves of one row tile each fit two workgroups per CU (four waves per
+// SIMD, at most 128 VGPRs); the other shapes run one.
 template <int D, int BLK, int RTW, int NS, int NW>
-__global__ __launch_bounds__(NW * kWave) void rectify_bf16_kernel(RectifyParams p) {
+__global__ __launch_bounds__(NW * kWave)
+__attribute__((amdgpu_waves_per_eu((RTW == 1 && NW == 8) ? BSA_RECTIFY_WAVES_PER_EU : 1)))
+void rectify_bf16_kernel(RectifyParams p) {
     constexpr int KS = D / 32;
     constexpr int NT = D / 16;
     constexpr int TILE_EL = 32 * D;             // elements of K (or V) per tile
     constexpr int CH = 2 * TILE_EL / 512;       // 1 KiB chunks per tile, K then V
     constexpr int CPW = CH / NW;                // chunks each wave copies
+    constexpr int RWG = 16 * RTW * NW;          // rows per workgroup (row group)
     static_assert(CPW >= 1 && CPW * NW == CH, "chunks split evenly over the waves");
     // NS-stage ring of tiles in LDS, filled by direct global->LDS copies
     // (copy16_to_lds): each wave copies CPW KiB chunks per tile, NS-1 tiles
     // ahead of the one being computed, without using registers.
     __shared__ __attribute__((aligned(16))) uint16_t ring[NS][2 * TILE_EL];
-    __shared__ int s_page[kChunkTiles * 32 / 32 + 2];
+    __shared__ int s_page[kMaxTilesPerWG * 32 / BLK + 2];
+    __shared__ long long s_loc[4];
 
     const CacheArgs& c = p.c;
     const RectifyArgs& a = p.a;
-    const int split = blockIdx.x;
-    const int grp = blockIdx.y;
-    const int s = grp / c.Hkv;
-    const int kvh = grp - s * c.Hkv;
     const int G = c.G;
     const int f = a.f;
     const int R = G * f;
-    const int T = c.seq_lens[s];
-    const int S = a.splits;
+    const int Z = (R + RWG - 1) / RWG;  // row groups per KV head
+    const int per_seq = c.Hkv * Z;
     const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 4;
-    const int col = lane & 15;
-    const int64_t row_base = (static_cast<int64_t>(s) * c.Hq + kvh * G) * f;  // output row of r = 0
-    const int rt0 = (blockIdx.z * NW + wave) * RTW;  // first 16-row tile of this wave
+    const int w = blockIdx.x;
 
-    const int ntiles = (T + 31) / 32;
-    const int t0 = split * a.chunk_tiles;
-    const int t1 = min(t0 + a.chunk_tiles, ntiles);
-    if (t0 >= t1) return;  // the merge only reads the chunks that cover [0, T)
-    const int nt = t1 - t0;
-
-    // page ids of the chunk's blocks (tiles are 32 tokens, blocks BLK tokens)
-    const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
-    const int blk0 = (32 * t0) / BLK;
-    const int nblk = (32 * (t1 - 1)) / BLK - blk0 + 1;
-    for (int i = threadIdx.x; i < nblk; i += NW * kWave) s_page[i] = ptrow[blk0 + i];
-
-    // B operand of S^T = K Q^T for each row tile: row rt*16 + col
-    bf16x8 qb[RTW][KS];
-    int pos[RTW];  // query position of the row held in column `col`
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-        const int r = (rt0 + rt) * 16 + col;
-        pos[rt] = (r < R) ? T - f + (r % f) : T - 1;
-        const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (row_base + r) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            u32x4 w = {0u, 0u, 0u, 0u};
-            if (r < R) w = ldg16(qp + ks * 32 + g * 8);
-            qb[rt][ks] = __builtin_bit_cast(bf16x8, w);
+    if (wave == 0) {
+        const SeqHit tot = seq_scan(c.seq_lens, c.B, per_seq, -1);
+        const int W = stream_wgs(tot.N, gridDim.x);
+        int64_t x0 = 0, x1 = 0;
+        SeqHit h{tot.N, -1, 0};
+        if (w < W) {
+            x0 = wg_begin(w, tot.N, W);
+            x1 = wg_begin(w + 1, tot.N, W);
+            h = seq_scan(c.seq_lens, c.B, per_seq, x0);
+        }
+        if ((threadIdx.x & 63) == 0) {
+            s_loc[0] = (w < W && x1 > x0) ? h.s : -1;
+            s_loc[1] = x0 - h.start;  // position inside sequence s's groups
+            s_loc[2] = x1 - x0;       // tiles of this workgroup
         }
     }
-    floatx4 oacc[RTW][NT];
-    float m_run[RTW], l_run[RTW];
-#pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-        m_run[rt] = -INFINITY;
-        l_run[rt] = 0.f;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) oacc[rt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
+    __syncthreads();
+    // (values read from LDS are wave-uniform; readfirstlane keeps them, and
+    // all the piece bookkeeping derived from them, in scalar registers)
+    int s = __builtin_amdgcn_readfirstlane(static_cast<int>(s_loc[0]));
+    if (s < 0) return;  // no tiles for this workgroup (uniform)
+    const int64_t pos0 = s_loc[1];
+    const int64_t left0 = s_loc[2];
+    int64_t left = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(left0 >> 32))) << 32) |
+                   static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(left0)));
+    int nts = ntiles_of(c.seq_lens[s]);
+    int gl = __builtin_amdgcn_readfirstlane(static_cast<int>(pos0 / nts));  // group inside the sequence
+    int off = __builtin_amdgcn_readfirstlane(static_cast<int>(pos0 - static_cast<int64_t>(gl) * nts));
 
     const uint16_t* kpool = static_cast<const uint16_t*>(c.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(c.v_pool);
     const float sl2 = a.scale_log2;
-    // retire the query and page-table loads before the copy ring starts, so
-    // that no wait for them lands inside the loop (where it would also drain
-    // the copies in flight)
-    wait_vmcnt<0>();
-    __syncthreads();  // s_page
+    const float rebase = kRebase / sl2;  // in raw score units
 
-    // queue the copies of tile t into ring stage buf
-    auto issue = [&](int t, int buf) __attribute__((always_inline)) {
-        const int tok0 = 32 * t;
-        const int blk = tok0 / BLK;
-        const int page = __builtin_amdgcn_readfirstlane(s_page[blk - blk0]);
-        const int64_t off = (static_cast<int64_t>(page) * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) +
-                            (tok0 - blk * BLK) * D + lane * 8;
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            const int ch = wave * CPW + i;
-            const uint16_t* src = (ch < CH / 2) ? kpool + off + ch * 512
-                                                : vpool + off + (ch - CH / 2) * 512;
-            copy16_to_lds(src, &ring[buf][ch * 512]);
-        }
-    };
+    while (true) {
+        // ---- one piece: tiles [t0, t1) of group (s, kvh, zg) ----
+        // The thread index is re-derived per piece behind an empty asm, so the
+        // compiler cannot hoist thread-dependent values (epilogue addresses,
+        // mask offsets) out of the piece loop, where they would stay live
+        // through the tile loop and cost registers.
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int g = lane >> 4;
+        const int col = lane & 15;
+        const int kvh = gl / Z;
+        const int zg = gl - kvh * Z;
+        const int T = c.seq_lens[s];
+        const int t0 = off;
+        const int nt = static_cast<int>(min(left, static_cast<int64_t>(nts - off)));
+        const int t1 = t0 + nt;
+        const int64_t slot = static_cast<int64_t>(s) * per_seq + gl + w;
+        const int64_t row_base = (static_cast<int64_t>(s) * c.Hq + kvh * G) * f;  // row r = 0
+        const int rt0 = (zg * NW + wave) * RTW;  // first 16-row tile of this wave
 
-#pragma unroll
-    for (int k = 0; k < NS - 1; ++k)
-        if (k < nt) issue(t0 + k, k);
-    for (int k = 0; k < nt; ++k) {
-        const int t = t0 + k;
-        const uint16_t* st = ring[k % NS];
-        // every wave is done reading the stage refilled next (it held tile k-1)
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-        if (k + NS - 1 < nt) {
-            issue(t + NS - 1, (k + NS - 1) % NS);
-            wait_vmcnt<CPW * (NS - 1)>();  // this wave's copies of tile k have landed
-        } else {
-            wait_vmcnt<0>();
-        }
-        __builtin_amdgcn_s_barrier();  // ... and every other wave's
-        asm volatile("" ::: "memory");  // no LDS read moves above this point
-    const uint16_t* ks_lds = st + lane * 8;
-        const uint16_t* vs_lds = st + TILE_EL + lane * 8;
-        u32x4 kr[2 * KS];
-#pragma unroll
-        for (int kk = 0; kk < 2 * KS; ++kk) kr[kk] = *reinterpret_cast<const u32x4*>(ks_lds + kk * 512);
-        u32x4 vr[NT];
-#pragma unroll
-        for (int n = 0; n < NT; ++n) vr[n] = *reinterpret_cast<const u32x4*>(vs_lds + n * 512);
-        const int tok0 = 32 * t;
-        const int nvalid = T - tok0;  // >= 1
-        if (nvalid < 32) {
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                const int tok = (kk < 4) ? (4 * g + kk) : (16 + 4 * g + kk - 4);
-                if (tok >= nvalid) {
-                    const uint32_t keep = (kk & 1) ? 0x0000ffffu : 0xffff0000u;
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) vr[n][kk >> 1] &= keep;
-                }
-            }
-        }
+        __syncthreads();  // the previous piece is done with s_page and the ring
+        // page ids of the piece's blocks (tiles are 32 tokens, blocks BLK tokens)
+        const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
+        const int blk0 = (32 * t0) / BLK;
+        const int nblk = (32 * (t1 - 1)) / BLK - blk0 + 1;
+        for (int i = tid; i < nblk; i += NW * kWave) s_page[i] = ptrow[blk0 + i];
+
+        // B operand of S^T = K Q^T for each row tile: row rt*16 + col
+        bf16x8 qb[RTW][KS];
+        int pos[RTW];  // query position of the row held in column `col`
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt) {
-            floatx4 sacc[2];
+            const int r = (rt0 + rt) * 16 + col;
+            pos[rt] = (r < R) ? T - f + (r % f) : T - 1;
+            const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (row_base + r) * D;
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, kr[mt * KS + ks]), qb[rt][ks], sacc[mt], 0, 0, 0);
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (r < R) v = ldg16(qp + ks * 32 + g * 8);
+                qb[rt][ks] = __builtin_bit_cast(bf16x8, v);
             }
-            float x[8];
+        }
+        floatx4 oacc[RTW][NT];
+        float m_run[RTW], l_run[RTW], nms[RTW];  // raw running max, sum, -max*scale
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) x[kk] = sacc[kk >> 2][kk & 3] * sl2;
-            if (tok0 + 31 > T - f) {  // the causal mask only bites in the last f tokens
+        for (int rt = 0; rt < RTW; ++rt) {
+            m_run[rt] = -INFINITY;
+            l_run[rt] = 0.f;
+            nms[rt] = 0.f;
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) {
-                    const int tok = tok0 + ((kk < 4) ? (4 * g + kk) : (16 + 4 * g + kk - 4));
-                    x[kk] = (tok <= pos[rt]) ? x[kk] : -INFINITY;
+            for (int n = 0; n < NT; ++n) oacc[rt][n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        }
+        // retire the query and page-table loads before the copy ring starts, so
+        // that no wait for them lands inside the loop (where it would also drain
+        // the copies in flight)
+        wait_vmcnt<0>();
+        __syncthreads();  // s_page
+
+        // queue the copies of tile t into ring stage buf
+        auto issue = [&](int t, int buf) __attribute__((always_inline)) {
+            const int tok0 = 32 * t;
+            const int blk = tok0 / BLK;
+            const int page = __builtin_amdgcn_readfirstlane(s_page[blk - blk0]);
+            const int64_t goff = (static_cast<int64_t>(page) * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) +
+                                 (tok0 - blk * BLK) * D + lane * 8;
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int ch = wave * CPW + i;
+                const uint16_t* src = (ch < CH / 2) ? kpool + goff + ch * 512
+                                                    : vpool + goff + (ch - CH / 2) * 512;
+                copy16_to_lds(src, &ring[buf][ch * 512]);
+            }
+        };
+
+#pragma unroll
+        for (int k = 0; k < NS - 1; ++k)
+            if (k < nt) issue(t0 + k, k);
+        for (int k = 0; k < nt; ++k) {
+            const int t = t0 + k;
+            const uint16_t* st = ring[k % NS];
+            // every wave is done reading the stage refilled next (it held tile k-1)
+            __builtin_amdgcn_s_barrier();
+            asm volatile("" ::: "memory");
+            if (k + NS - 1 < nt) {
+                issue(t + NS - 1, (k + NS - 1) % NS);
+                wait_vmcnt<CPW * (NS - 1)>();  // this wave's copies of tile k have landed
+            } else {
+                wait_vmcnt<0>();
+            }
+            __builtin_amdgcn_s_barrier();  // ... and every other wave's
+            asm volatile("" ::: "memory");  // no LDS read moves above this point
+            const uint16_t* ks_lds = st + lane * 8;
+            const uint16_t* vs_lds = st + TILE_EL + lane * 8;
+            u32x4 kr[2 * KS];
+#pragma unroll
+            for (int kk = 0; kk < 2 * KS; ++kk) kr[kk] = *reinterpret_cast<const u32x4*>(ks_lds + kk * 512);
+            const int tok0 = 32 * t;
+            const int nvalid = T - tok0;  // >= 1
+            u32x4 vr[NT];
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) {
+                floatx4 sacc[2];
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) {
+                    sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks)
+                        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, kr[mt * KS + ks]), qb[rt][ks], sacc[mt], 0, 0, 0);
                 }
-            }
-            float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                               fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            if (__ballot(tmax > m_run[rt]) != 0) {  // some row's running max grows
-                const float m_new = fmaxf(m_run[rt], tmax);
-                const float alpha = __builtin_amdgcn_exp2f(m_run[rt] - m_new);
-                l_run[rt] *= alpha;
-                m_run[rt] = m_new;
-                float al[4];
+                if (rt == 0) {
+                    // V operands are read once the K operands are consumed, which
+                    // keeps both out of registers at the same time
+                    asm volatile("" ::: "memory");
 #pragma unroll
-                for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * g + e, 64);
+                    for (int n = 0; n < NT; ++n) vr[n] = *reinterpret_cast<const u32x4*>(vs_lds + n * 512);
+                    if (nvalid < 32) {  // zero V of the tokens past T (ragged last tile)
+#pragma unroll
+                        for (int kk = 0; kk < 8; ++kk) {
+                            const int tok = (kk < 4) ? (4 * g + kk) : (16 + 4 * g + kk - 4);
+                            if (tok >= nvalid) {
+                                const uint32_t keep = (kk & 1) ? 0x0000ffffu : 0xffff0000u;
+#pragma unroll
+                                for (int n = 0; n < NT; ++n) vr[n][kk >> 1] &= keep;
+                            }
+                        }
+                    }
+                }
+                // raw scores; the scale is folded into the exponent below
+                float x[8];
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) x[kk] = sacc[kk >> 2][kk & 3];
+                if (tok0 + 31 > T - f) {  // the causal mask only bites in the last f tokens
+#pragma unroll
+                    for (int kk = 0; kk < 8; ++kk) {
+                        const int tok = tok0 + ((kk < 4) ? (4 * g + kk) : (16 + 4 * g + kk - 4));
+                        x[kk] = (tok <= pos[rt]) ? x[kk] : -INFINITY;
+                    }
+                }
+                float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                   fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+                tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+                // The reference point of the exponentials moves only when a row's
+                // score exceeds it by more than kRebase (log2 units), so most tiles
+                // skip the accumulator rescale; p stays below 2^kRebase, which the
+                // fp32 sums and the bf16 P operand carry without loss of range.
+                if (__ballot(tmax > m_run[rt] + rebase) != 0) {
+                    const float m_new = fmaxf(m_run[rt], tmax);
+                    // a row that has seen nothing keeps its (zero) state
+                    const float alpha = (m_new == -INFINITY)
+                                            ? 1.f
+                                            : __builtin_amdgcn_exp2f((m_run[rt] - m_new) * sl2);
+                    l_run[rt] *= alpha;
+                    m_run[rt] = m_new;
+                    nms[rt] = (m_new == -INFINITY) ? 0.f : -m_new * sl2;
+                    float al[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) al[e] = __shfl(alpha, 4 * g + e, 64);
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) oacc[rt][n][e] *= al[e];
+                }
+                float pr[8];
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) pr[kk] = __builtin_amdgcn_exp2f(fmaf(x[kk], sl2, nms[rt]));
+                l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+                bf16x8 ph;
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) ph[kk] = static_cast<__bf16>(pr[kk]);
 #pragma unroll
                 for (int n = 0; n < NT; ++n)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) oacc[rt][n][e] *= al[e];
+                    oacc[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        ph, __builtin_bit_cast(bf16x8, vr[n]), oacc[rt][n], 0, 0, 0);
             }
-            const float m_use = (m_run[rt] == -INFINITY) ? 0.f : m_run[rt];  // row sees nothing yet
-            float pr[8];
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) pr[kk] = __builtin_amdgcn_exp2f(x[kk] - m_use);
-            l_run[rt] += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-            bf16x8 ph, pl;
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) ph[kk] = static_cast<__bf16>(pr[kk]);
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-                pl[kk] = static_cast<__bf16>(pr[kk] - static_cast<float>(ph[kk]));
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const bf16x8 vb = __builtin_bit_cast(bf16x8, vr[n]);
-                oacc[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, oacc[rt][n], 0, 0, 0);
-                oacc[rt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, oacc[rt][n], 0, 0, 0);
-            }
-        }    }
+        }
 
-    // partials for this wave's rows
+        // partials of this wave's rows for the piece, in slot `slot`
 #pragma unroll
-    for (int rt = 0; rt < RTW; ++rt) {
-        float l_tot = l_run[rt] + __shfl_xor(l_run[rt], 16, 64);
-        l_tot += __shfl_xor(l_tot, 32, 64);
+        for (int rt = 0; rt < RTW; ++rt) {
+            float l_tot = l_run[rt] + __shfl_xor(l_run[rt], 16, 64);
+            l_tot += __shfl_xor(l_tot, 32, 64);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int rr = 4 * g + e;  // row inside the tile held in element e
-            const float L = __shfl(l_tot, rr, 64);
-            const float M = __shfl(m_run[rt], rr, 64);
-            const int r = (rt0 + rt) * 16 + rr;
-            if (r >= R) continue;
-            const int64_t row = row_base + r;
-            float* op = a.o_part + (row * S + split) * D;
-            const bool empty = (M == -INFINITY);
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 4 * g + e;  // row inside the tile held in element e
+                const float L = __shfl(l_tot, rr, 64);
+                const float M = __shfl(m_run[rt], rr, 64);
+                const int r = (rt0 + rt) * 16 + rr;
+                if (r >= R) continue;
+                const int64_t prow = slot * RWG + (r - zg * RWG);
+                float* op = a.o_part + prow * D;
+                const bool empty = (M == -INFINITY);
 #pragma unroll
-            for (int n = 0; n < NT; ++n) op[n * 16 + col] = empty ? 0.f : oacc[rt][n][e] / L;
-            if (col == 0) a.lse_part[row * S + split] = empty ? -INFINITY : M + log2f(L);
+                for (int n = 0; n < NT; ++n) op[n * 16 + col] = empty ? 0.f : oacc[rt][n][e] / L;
+                if (col == 0) a.lse_part[prow] = empty ? -INFINITY : M * sl2 + log2f(L);
+            }
+        }
+
+        // ---- next piece ----
+        left -= nt;
+        if (left <= 0) break;
+        off = 0;
+        if (++gl == per_seq) {
+            gl = 0;
+            do {
+                ++s;
+                nts = ntiles_of(c.seq_lens[s]);
+            } while (nts == 0);  // tiles remain, so a non-empty sequence follows
         }
     }
+}
+
+// Merge of the pieces of every row of the bf16 path, in list order.  One
+// workgroup per 16 rows of a row group: 16 threads per row, each owning d/16
+// channels; the row's pieces (one partial per slot, RWG partial rows apart)
+// are read four at a time and weighted by 2^(lse_k - M).
+template <int RWG, int D>
+__global__ __launch_bounds__(256) void rectify_merge_kernel(RectifyParams p) {
+    constexpr int CPT = D / 16;  // channels per thread
+    static_assert(CPT % 4 == 0, "float4 channel groups");
+    __shared__ long long s_loc[2];
+    const CacheArgs& c = p.c;
+    const RectifyArgs& a = p.a;
+    const int R = c.G * a.f;
+    const int Z = (R + RWG - 1) / RWG;
+    const int per_seq = c.Hkv * Z;
+    const int nrb = (R + 15) / 16;
+    const int grp = blockIdx.x / nrb;  // s * Hkv + kvh
+    const int r0 = (blockIdx.x - grp * nrb) * 16;
+    const int s = grp / c.Hkv;
+    const int kvh = grp - s * c.Hkv;
+    const int zg = r0 / RWG;  // the 16 rows share a row group (RWG is a multiple of 16)
+    const int tid = threadIdx.x;
+    if (tid < kWave) {
+        const SeqHit tot = seq_scan(c.seq_lens, c.B, per_seq, -1);
+        const SeqHit pre = seq_scan(c.seq_lens, s, per_seq, -1);  // tiles of sequences < s
+        if (tid == 0) {
+            s_loc[0] = tot.N;
+            s_loc[1] = pre.N;
+        }
+    }
+    __syncthreads();
+    const int64_t N = s_loc[0];
+    const int nts = ntiles_of(c.seq_lens[s]);
+    const int W = stream_wgs(N, a.wgs);
+    const int gl = kvh * Z + zg;
+    const int64_t start = s_loc[1] + static_cast<int64_t>(gl) * nts;
+    int w0 = 0, npieces = 0;
+    if (nts > 0) {
+        w0 = wg_owner(start, N, W);
+        npieces = wg_owner(start + nts - 1, N, W) - w0 + 1;
+    }
+    const int row = tid >> 4;
+    const int q = tid & 15;
+    const int r = r0 + row;
+    const bool valid = r < R;
+    const int64_t prow0 = (static_cast<int64_t>(s) * per_seq + gl + w0) * RWG + (r - zg * RWG);
+    const float* lp = a.lse_part + prow0;
+    float M = -INFINITY;
+    if (valid)
+        for (int k = q; k < npieces; k += 16) M = fmaxf(M, lp[static_cast<int64_t>(k) * RWG]);
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 16));
+    float acc[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) acc[i] = 0.f;
+    float L = 0.f;
+    if (valid && M != -INFINITY) {
+        const float* op = a.o_part + prow0 * D + q * CPT;
+        for (int k0 = 0; k0 < npieces; k0 += 4) {
+            float lv[4];
+            floatx4 ov[4][CPT / 4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t k = k0 + u;
+                lv[u] = -INFINITY;
+                if (k < npieces) {
+                    lv[u] = lp[k * RWG];
+#pragma unroll
+                    for (int v = 0; v < CPT / 4; ++v)
+                        ov[u][v] = *reinterpret_cast<const floatx4*>(op + k * RWG * D + 4 * v);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                if (k0 + u >= npieces) break;
+                const float wk = exp2f(lv[u] - M);
+                L += wk;
+#pragma unroll
+                for (int v = 0; v < CPT / 4; ++v)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[4 * v + e] += wk * ov[u][v][e];
+            }
+        }
+    }
+    if (!valid) return;
+    const bool empty = (M == -INFINITY);
+    const int64_t orow = (static_cast<int64_t>(s) * c.Hq + kvh * c.G) * a.f + r;
+    typedef typename Elem<kBF16>::T E;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+        Elem<kBF16>::store(static_cast<E*>(a.o), orow * D + q * CPT + i, empty ? 0.f : acc[i] / L);
+    if (q == 0) a.lse[orow] = empty ? -INFINITY : (M + log2f(L)) * kLn2;
 }
 
 // fp32 caches: one wave per row at a time, lane t < 32 owns token t of a tile.
@@ -352,19 +588,27 @@ __global__ __launch_bounds__(kThreads) void rectify_f32_kernel(RectifyParams p) 
     }
 }
 
+// Rows (G*f) per workgroup: up to 64 with 4 waves, up to 128 with 8 waves of
+// one 16-row tile each (two waves per SIMD), 256 with 8 waves of two tiles;
+// more rows take several row groups.
+int rows_per_wg(int R) { return R <= 64 ? 64 : (R <= 128 ? 128 : 256); }
+
 template <int D, int BLK, int RTW, int NW>
 hipError_t launch_bf16(const RectifyParams& p, hipStream_t stream) {
+    constexpr int RWG = 16 * RTW * NW;
+    if (p.a.rows_per_wg != RWG) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((rectify_bf16_kernel<D, BLK, RTW, kStages, NW>), dim3(p.a.wgs),
+                       dim3(NW * kWave), 0, stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
     const int R = p.c.G * p.a.f;
-    const int rows_per_wg = 16 * RTW * NW;
-    dim3 grid(p.a.splits, p.c.B * p.c.Hkv, (R + rows_per_wg - 1) / rows_per_wg);
-    hipLaunchKernelGGL((rectify_bf16_kernel<D, BLK, RTW, kStages, NW>), grid, dim3(NW * kWave), 0,
-                       stream, p);
+    const int64_t wgs = static_cast<int64_t>(p.c.B) * p.c.Hkv * ((R + 15) / 16);
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((rectify_merge_kernel<RWG, D>), dim3(static_cast<uint32_t>(wgs)), dim3(256),
+                       0, stream, p);
     return hipGetLastError();
 }
 
-// Rows (G*f) per workgroup: up to 64 with 4 waves, up to 128 with 8 waves of
-// one 16-row tile each (two waves per SIMD), 256 with 8 waves of two tiles;
-// more rows take several workgroups along z.
 template <int D, int BLK>
 hipError_t launch_bf16_r(const RectifyParams& p, hipStream_t stream) {
     const int R = p.c.G * p.a.f;
@@ -395,26 +639,41 @@ hipError_t launch_f32(const RectifyParams& p, hipStream_t stream) {
 
 }  // namespace
 
-void rectify_splits(const CacheArgs& c, int f, int* splits, int* chunk_tiles) {
-    (void)f;
+void rectify_plan(const CacheArgs& c, int f, RectifyPlan* pl) {
     const int64_t max_tokens = static_cast<int64_t>(c.max_blocks) * c.block;
     const int64_t tiles = (max_tokens + 31) / 32;
-    *chunk_tiles = kChunkTiles;
-    *splits = static_cast<int>((tiles + kChunkTiles - 1) / kChunkTiles);
+    *pl = RectifyPlan{};
+    if (c.dtype == kBF16) {
+        const int R = c.G * f;
+        const int rwg = rows_per_wg(R);
+        const int64_t groups = static_cast<int64_t>(c.B) * c.Hkv * ((R + rwg - 1) / rwg);
+        const int64_t n_max = groups * tiles;
+        const int64_t wgs = std::max<int64_t>(kStreamWGs, (n_max + kMaxTilesPerWG - 1) / kMaxTilesPerWG);
+        pl->wgs = static_cast<int>(std::min<int64_t>(wgs, 0x7fffffff));
+        pl->rows_per_wg = rwg;
+        const int64_t slots = groups + wgs;
+        pl->o_floats = slots * rwg * c.d;
+        pl->lse_floats = slots * rwg;
+    } else {
+        pl->chunk_tiles = kChunkTiles;
+        pl->splits = static_cast<int>((tiles + kChunkTiles - 1) / kChunkTiles);
+        const int64_t rows = static_cast<int64_t>(c.B) * c.Hq * f;
+        pl->o_floats = rows * pl->splits * c.d;
+        pl->lse_floats = rows * pl->splits;
+    }
 }
 
 hipError_t launch_rectify(const CacheArgs& c, const RectifyArgs& a, hipStream_t stream) {
     // 1. overwrite [T-f, T) and rebuild the descriptors of the blocks it touches
     hipError_t err = launch_kv_write(c, kModeOverwrite, a.k_new, a.v_new, a.f, nullptr, stream);
     if (err != hipSuccess) return err;
-    // 2. causal dense attention, split over token chunks
     RectifyParams p{c, a};
-    if (c.dtype == kBF16)
-        err = c.d == 64 ? launch_bf16_d<64>(p, stream) : launch_bf16_d<128>(p, stream);
-    else
-        err = c.d == 64 ? launch_f32<64>(p, stream) : launch_f32<128>(p, stream);
+    // 2. causal dense attention over even shares of all tiles, then the merge
+    if (c.dtype == kBF16) return c.d == 64 ? launch_bf16_d<64>(p, stream) : launch_bf16_d<128>(p, stream);
+    // fp32: chunks of kChunkTiles tiles, then the merge of the chunks covering
+    // [0, T) of each sequence
+    err = c.d == 64 ? launch_f32<64>(p, stream) : launch_f32<128>(p, stream);
     if (err != hipSuccess) return err;
-    // 3. merge the chunks (only the chunks covering [0, T) of each sequence)
     return launch_combine_ragged(c.dtype, c.d, c.B * c.Hq * a.f, a.splits, a.o_part, a.lse_part,
                                  a.o, a.lse, c.seq_lens, c.Hq * a.f, 32 * a.chunk_tiles, stream);
 }

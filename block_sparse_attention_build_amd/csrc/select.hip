@@ -191,15 +191,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     for (int m = 32; m >= 1; m >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, 64)));
     return v;
 }
-__device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    return x;
-}
 
 struct TopnParams {
     CacheArgs c;
