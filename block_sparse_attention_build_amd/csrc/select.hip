@@ -139,23 +139,49 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
             wv[e] = acc;
         }
     } else {
-        // u = sum_h q_h (once, in LDS), then w = W u for this lane's channels
+        // u = sum_h q_h, then w = W u, both in LDS: kScoreThreads / D threads
+        // per output channel, each a 16-byte-load dot product over its share
+        // of the row, then the shares added in fixed order
+        constexpr int PARTS = kScoreThreads / D;
+        constexpr int KP = D / PARTS;
+        static_assert(PARTS * D == kScoreThreads && KP % 8 == 0, "gate matvec split");
         __shared__ float u_s[D];
+        __shared__ float w_part[kScoreThreads];
+        __shared__ float w_s[D];
         for (int i = tid; i < D; i += kScoreThreads) {
             float acc = 0.f;
             for (int h = 0; h < c.G; ++h) acc += qs[h * D + i];
             u_s[i] = acc;
         }
         __syncthreads();
-        const uint16_t* W = static_cast<const uint16_t*>(a.gate_w);
+        {
+            const int r = tid % D;
+            const int part = tid / D;
+            const uint16_t* wr = static_cast<const uint16_t*>(a.gate_w) + r * D + part * KP;
+            u32x4 wl[KP / 8];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const uint16_t* wr = W + (ch0 + e) * D;
+            for (int k = 0; k < KP / 8; ++k) wl[k] = *reinterpret_cast<const u32x4*>(wr + 8 * k);
             float acc = 0.f;
-#pragma unroll 4
-            for (int k = 0; k < D; ++k) acc += bf2f(wr[k]) * u_s[k];
-            wv[e] = acc;
+#pragma unroll
+            for (int k = 0; k < KP / 8; ++k)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float* uu = u_s + part * KP + 8 * k + 2 * e;
+                    acc += __uint_as_float(wl[k][e] << 16) * uu[0];
+                    acc += __uint_as_float(wl[k][e] & 0xffff0000u) * uu[1];
+                }
+            w_part[tid] = acc;
         }
+        __syncthreads();
+        if (tid < D) {
+            float acc = 0.f;
+#pragma unroll
+            for (int pp = 0; pp < PARTS; ++pp) acc += w_part[pp * D + tid];
+            w_s[tid] = acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) wv[e] = w_s[ch0 + e];
     }
 
     float part[kScoreIters];
