@@ -66,6 +66,25 @@ def kv_bytes(w, T, n):
     return w.Hkv * NB * desc_per_block, w.Hkv * tokens * 2 * d * es
 
 
+def bench_layout(w, sparsities=None, gate=None):
+    """The cache layout and selection parameters the benchmark launches with
+    (capacity = the longest context + 4096 tokens of decode headroom; idx
+    rows sized for the largest kept count the capacity allows).  Returns
+    (layout, {sparsity_bp: params})."""
+    import block_sparse_attention_build_amd as bsa
+    cap_tokens = max(w.T0) + 4096
+    max_blocks = (cap_tokens + w.block - 1) // w.block
+    kv = bsa.DTYPE_BF16 if w.dtype == "bf16" else bsa.DTYPE_F32
+    L = bsa.Layout(w.B, w.Hq, w.Hkv, w.d, w.block, max_blocks, kv, w.desc_kind)
+    params = {}
+    for bp in (sparsities or [w.sparsity_bp]):
+        P = bsa.SelectParams(budget_tokens=w.budget_tokens, sparsity_bp=bp, n_local=w.n_local,
+                             n_min=w.n_min, gate_w=gate)
+        P.n_max = bsa.block_count(P, max_blocks, w.block)
+        params[bp] = P
+    return L, params
+
+
 class Run:
     """L layer caches of one workload, ready for decode steps."""
 
@@ -76,10 +95,6 @@ class Run:
         self.w, self.layers, self.dev, self.bsa = w, layers, dev, bsa
         self.T0 = list(w.T0)
         self.steps_done = 0
-        cap_tokens = max(self.T0) + 4096
-        max_blocks = (cap_tokens + w.block - 1) // w.block
-        kv = bsa.DTYPE_BF16 if w.dtype == "bf16" else bsa.DTYPE_F32
-        self.L = bsa.Layout(w.B, w.Hq, w.Hkv, w.d, w.block, max_blocks, kv, w.desc_kind)
         self.tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         gate = None
         if w.desc_kind == W.DESC_MEANPOOL:
@@ -87,12 +102,9 @@ class Run:
             g.manual_seed(w.seed(0) + 7)
             gate = (torch.randn(w.d, w.d, device=dev, generator=g) / math.sqrt(w.d)).to(torch.bfloat16)
         sps = sparsities or [w.sparsity_bp]
-        self.params = {}
-        for bp in sps:
-            P = bsa.SelectParams(budget_tokens=w.budget_tokens, sparsity_bp=bp, n_local=w.n_local,
-                                 n_min=w.n_min, gate_w=gate)
-            P.n_max = bsa.block_count(P, max_blocks, w.block)
-            self.params[bp] = P
+        self.L, self.params = bench_layout(w, sps, gate)
+        max_blocks = self.L.max_blocks
+        kv = self.L.kv_dtype
         self.P = self.params[sps[0]]
         n_max_all = max(P.n_max for P in self.params.values())
         self.seq_lens = torch.zeros(w.B, dtype=torch.int32, device=dev)

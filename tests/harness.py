@@ -173,11 +173,13 @@ def gap_direction(L, qg, W_gate):
 
 
 def enforce_gap(L, params, q, Ks, lengths_per_step, W_gate=None, rel=1e-3, max_iter=30,
-                on_shift=None):
+                on_shift=None, groups=None):
     """Make the top-n boundary clear-cut at every checked step.
 
-    Ks[s]: [Hkv, T_total, d] float32 (exact stored values; modified in place).
+    Ks[s]: [Hkv, T_total, d] float32 (exact stored values; modified in place),
+    or a dict {kv head: [T_total, d]} holding only the checked heads.
     lengths_per_step[s]: the cache lengths T at which selection is checked.
+    groups: optional set of (s, kv head) to enforce; default all.
     The candidates at length T are the full blocks 0..NB-n_local'-1, which no
     later append changes, so one score array at the final length serves all
     steps.  A violated boundary (gap < rel * max(1, |s|, term magnitude))
@@ -193,6 +195,8 @@ def enforce_gap(L, params, q, Ks, lengths_per_step, W_gate=None, rel=1e-3, max_i
         for s, steps in enumerate(lengths_per_step):
             Tmax = max(steps)
             for h in range(L.Hkv):
+                if groups is not None and (s, h) not in groups:
+                    continue
                 qg = q[s, h * G:(h + 1) * G]
                 NBf = Tmax // b
                 sc, mag = _scores_and_mag(L, qg, Ks[s][h], NBf * b, W_gate)
@@ -222,7 +226,7 @@ def enforce_gap(L, params, q, Ks, lengths_per_step, W_gate=None, rel=1e-3, max_i
                     delta = max(4.0 * (need - (s_in - s_out)) / grad, 0.25 * (1 + it))
                     for j in order[:k]:
                         t0, t1 = j * b, (j + 1) * b
-                        Ks[s][h, t0:t1] = W.quantize(Ks[s][h, t0:t1] + delta * u,
+                        Ks[s][h][t0:t1] = W.quantize(Ks[s][h][t0:t1] + delta * u,
                                                      "bf16" if L.kv_dtype == bsa.DTYPE_BF16
                                                      else "f32")
                         if on_shift:
