@@ -98,25 +98,84 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
+// ---------------------------------------------------------------------------
+// DPP wave primitives (GFX9 data-parallel primitives: row_shr:n moves a value
+// n lanes up inside each row of 16 lanes, row_bcast:15 hands lane 15 of a row
+// to the next row, row_bcast:31 hands lane 31 to rows 2 and 3).  They run
+// on the VALU with no LDS round trip, unlike the generic lane shuffles.
+// Lanes with no source keep `old`, which is the operation's identity.
+// ---------------------------------------------------------------------------
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp_move(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    x += dpp_move<kDppRowShr1, 0xf>(0, x);
+    x += dpp_move<kDppRowShr2, 0xf>(0, x);
+    x += dpp_move<kDppRowShr4, 0xf>(0, x);
+    x += dpp_move<kDppRowShr8, 0xf>(0, x);
+    x += dpp_move<kDppRowBcast15, 0xa>(0, x);
+    x += dpp_move<kDppRowBcast31, 0xc>(0, x);
     return x;
+}
+
+// Sum of float v over each run of W consecutive lanes (W = 16, 32 or 64),
+// left in the run's last lane (the other lanes hold partial sums).
+template <int W>
+__device__ __forceinline__ float group_sum_last(float v) {
+    static_assert(W == 16 || W == 32 || W == 64, "run width");
+    auto add = [](float a, int b) { return a + __int_as_float(b); };
+    v = add(v, dpp_move<kDppRowShr1, 0xf>(0, __float_as_int(v)));
+    v = add(v, dpp_move<kDppRowShr2, 0xf>(0, __float_as_int(v)));
+    v = add(v, dpp_move<kDppRowShr4, 0xf>(0, __float_as_int(v)));
+    v = add(v, dpp_move<kDppRowShr8, 0xf>(0, __float_as_int(v)));
+    if (W >= 32) v = add(v, dpp_move<kDppRowBcast15, 0xa>(0, __float_as_int(v)));
+    if (W >= 64) v = add(v, dpp_move<kDppRowBcast31, 0xc>(0, __float_as_int(v)));
+    return v;
+}
+
+// Minimum / maximum of an unsigned value over the wave, returned to every lane.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    int x = static_cast<int>(v);
+    auto mn = [](int a, int b) { return static_cast<int>(min(static_cast<uint32_t>(a), static_cast<uint32_t>(b))); };
+    x = mn(x, dpp_move<kDppRowShr1, 0xf>(x, x));
+    x = mn(x, dpp_move<kDppRowShr2, 0xf>(x, x));
+    x = mn(x, dpp_move<kDppRowShr4, 0xf>(x, x));
+    x = mn(x, dpp_move<kDppRowShr8, 0xf>(x, x));
+    x = mn(x, dpp_move<kDppRowBcast15, 0xa>(x, x));
+    x = mn(x, dpp_move<kDppRowBcast31, 0xc>(x, x));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    int x = static_cast<int>(v);
+    auto mx = [](int a, int b) { return static_cast<int>(max(static_cast<uint32_t>(a), static_cast<uint32_t>(b))); };
+    x = mx(x, dpp_move<kDppRowShr1, 0xf>(x, x));
+    x = mx(x, dpp_move<kDppRowShr2, 0xf>(x, x));
+    x = mx(x, dpp_move<kDppRowShr4, 0xf>(x, x));
+    x = mx(x, dpp_move<kDppRowShr8, 0xf>(x, x));
+    x = mx(x, dpp_move<kDppRowBcast15, 0xa>(x, x));
+    x = mx(x, dpp_move<kDppRowBcast31, 0xc>(x, x));
+    return static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 63));
+}
+// Maximum / sum of a float over the wave, returned to every lane.
+__device__ __forceinline__ float wave_max(float v) {
+    auto mx = [](float a, int b) { return fmaxf(a, __int_as_float(b)); };
+    v = mx(v, dpp_move<kDppRowShr1, 0xf>(__float_as_int(v), __float_as_int(v)));
+    v = mx(v, dpp_move<kDppRowShr2, 0xf>(__float_as_int(v), __float_as_int(v)));
+    v = mx(v, dpp_move<kDppRowShr4, 0xf>(__float_as_int(v), __float_as_int(v)));
+    v = mx(v, dpp_move<kDppRowShr8, 0xf>(__float_as_int(v), __float_as_int(v)));
+    v = mx(v, dpp_move<kDppRowBcast15, 0xa>(__float_as_int(v), __float_as_int(v)));
+    v = mx(v, dpp_move<kDppRowBcast31, 0xc>(__float_as_int(v), __float_as_int(v)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v = group_sum_last<64>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Order-preserving map of fp32 to uint32 (larger float -> larger key);

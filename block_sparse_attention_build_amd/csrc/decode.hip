@@ -397,21 +397,24 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeParams p) {
 // Merge of the partial (o, base-2 lse) pairs of each row, in a fixed order.
 // Row `row` merges its first S splits, or, when seq_lens is given, only the
 // splits that cover [0, seq_lens[row / rows_per_seq]) at tokens_per_split
-// tokens each (the others were never written).  Grid: rows x (d / 64); a
-// workgroup puts the split weights 2^(lse_k - M) in LDS, then its 256 threads
-// take 64 channels x 4 split lanes, each lane summing every 4th split with 8
-// independent loads in flight, and the 4 lane sums are added in fixed order.
+// tokens each (the others were never written).  Grid: rows x (d / 64); the
+// 256 threads take 64 channels x 4 split lanes.  Every partial o a thread
+// needs is loaded in the same round trip as the lse values (kCombBatch per
+// lane at a time); the split weights 2^(lse_k - M) are formed once M is
+// known, and the 4 lane sums (o and weights) are added in fixed order.
 constexpr int kCombThreads = 256;
-constexpr int kCombCh = 64;                        // channels per workgroup
+constexpr int kCombCh = 64;                         // channels per workgroup
 constexpr int kCombLanes = kCombThreads / kCombCh;  // split lanes per channel
+constexpr int kCombBatch = 16;                      // o loads in flight per lane
 
 template <int DT>
 __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     int d, int S, const float* __restrict__ o_part, const float* __restrict__ lse_part, void* o,
     float* lse, const int32_t* seq_lens, int rows_per_seq, int tokens_per_split) {
-    extern __shared__ float wts[];  // [S] weights
+    extern __shared__ float lse_s[];  // [S] partial lse of the row
     __shared__ float red[kCombThreads / kWave];
     __shared__ float part_sum[kCombLanes][kCombCh];
+    __shared__ float part_w[kCombLanes];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
     int Sv = S;
@@ -419,11 +422,22 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
         const int T = seq_lens[row / rows_per_seq];
         Sv = min(S, (T + tokens_per_split - 1) / tokens_per_split);
     }
+    const int cl = tid % kCombCh;
+    const int lane_k = tid / kCombCh;
+    const int ch = blockIdx.y * kCombCh + cl;
+    const float* op = o_part + row * S * d + ch;
     const float* lp = lse_part + row * S;
+    // first batch of partial o values, in flight together with the lse loads
+    float ov[kCombBatch];
+#pragma unroll
+    for (int u = 0; u < kCombBatch; ++u) {
+        const int k = lane_k + kCombLanes * u;
+        ov[u] = (k < Sv) ? op[static_cast<int64_t>(k) * d] : 0.f;
+    }
     float m = -INFINITY;
     for (int k = tid; k < Sv; k += kCombThreads) {
         const float v = lp[k];
-        wts[k] = v;
+        lse_s[k] = v;
         m = fmaxf(m, v);
     }
     m = wave_max(m);
@@ -432,38 +446,37 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kCombThreads / kWave; ++w) M = fmaxf(M, red[w]);
-    __syncthreads();
-    float lsum = 0.f;
-    for (int k = tid; k < Sv; k += kCombThreads) {
-        const float wk = (M == -INFINITY) ? 0.f : exp2f(wts[k] - M);
-        wts[k] = wk;
-        lsum += wk;
-    }
-    lsum = wave_sum(lsum);
-    if ((tid & 63) == 0) red[tid >> 6] = lsum;
-    __syncthreads();
-    float L = 0.f;
+    float acc = 0.f, wsum = 0.f;
+    if (M != -INFINITY) {
+        for (int k0 = 0; k0 < Sv; k0 += kCombLanes * kCombBatch) {
+            if (k0 > 0) {  // more splits than one batch covers
 #pragma unroll
-    for (int w = 0; w < kCombThreads / kWave; ++w) L += red[w];
-    const int cl = tid % kCombCh;
-    const int lane_k = tid / kCombCh;
-    const int ch = blockIdx.y * kCombCh + cl;
-    const float* op = o_part + row * S * d + ch;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    int k = lane_k;
-    for (; k + 7 * kCombLanes < Sv; k += 8 * kCombLanes) {
+                for (int u = 0; u < kCombBatch; ++u) {
+                    const int k = k0 + lane_k + kCombLanes * u;
+                    ov[u] = (k < Sv) ? op[static_cast<int64_t>(k) * d] : 0.f;
+                }
+            }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            acc[u] += wts[k + u * kCombLanes] * op[static_cast<int64_t>(k + u * kCombLanes) * d];
+            for (int u = 0; u < kCombBatch; ++u) {
+                const int k = k0 + lane_k + kCombLanes * u;
+                if (k < Sv) {
+                    const float wk = exp2f(lse_s[k] - M);
+                    acc += wk * ov[u];
+                    wsum += wk;
+                }
+            }
+        }
     }
-    for (; k < Sv; k += kCombLanes) acc[0] += wts[k] * op[static_cast<int64_t>(k) * d];
-    part_sum[lane_k][cl] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) +
-                           ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    part_sum[lane_k][cl] = acc;
+    if (cl == 0) part_w[lane_k] = wsum;
     __syncthreads();
     if (lane_k == 0) {
-        float tot = 0.f;
+        float tot = 0.f, L = 0.f;
 #pragma unroll
-        for (int p2 = 0; p2 < kCombLanes; ++p2) tot += part_sum[p2][cl];
+        for (int p2 = 0; p2 < kCombLanes; ++p2) {
+            tot += part_sum[p2][cl];
+            L += part_w[p2];
+        }
         const bool empty = (M == -INFINITY);
         Elem<DT>::store(static_cast<typename Elem<DT>::T*>(o), row * d + ch, empty ? 0.f : tot / L);
         if (ch == 0) lse[row] = empty ? -INFINITY : (M + log2f(L)) * kLn2;

@@ -33,9 +33,13 @@ namespace bsa {
 namespace {
 
 constexpr int kScoreThreads = 256;
-constexpr int kScoreIters = 8;
+#ifndef BSA_SCORE_ITERS
+#define BSA_SCORE_ITERS 8
+#endif
+constexpr int kScoreIters = BSA_SCORE_ITERS;
 constexpr int kTopnThreads = 1024;
 constexpr int kTopnWaves = kTopnThreads / kWave;
+constexpr int kAliveCap = 2048;  // keys gathered after the first radix pass
 
 struct ScoreParams {
     CacheArgs c;
@@ -195,9 +199,9 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
     float* out = a.scores + static_cast<int64_t>(grp) * p.stride;
 #pragma unroll
     for (int it = 0; it < kScoreIters; ++it) {
-        const float tot = group_sum<LPB>(part[it]);
+        const float tot = group_sum_last<LPB>(part[it]);
         const int j = c0 + (it * (kScoreThreads / kWave) + wave) * BPL + bl;
-        if (lp == 0 && j < NC) {
+        if (lp == LPB - 1 && j < NC) {
             float v = tot;
             if (DESC == kMeanPool) v = v / static_cast<float>(min(c.block, T - j * c.block));
             out[j] = v;
@@ -206,17 +210,6 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
 }
 
 // ----------------------------- top-n ---------------------------------------
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, 64)));
-    return v;
-}
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), m, 64)));
-    return v;
-}
 
 struct TopnParams {
     CacheArgs c;
@@ -228,11 +221,14 @@ template <int KPT>
 __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     const CacheArgs& c = p.c;
     const SelectArgs& a = p.s;
-    // three rotating histograms: pass k counts into hist[k%3] and clears
-    // hist[(k+1)%3], which nobody reads any more (its pass ended two
-    // barriers ago), so every radix pass needs a single barrier
-    __shared__ int hist[3][256];
+    // one private histogram per wave (LDS atomics then only collide within
+    // a wave instruction, not across the 16 waves), summed into hsum
+    __shared__ int hist[kTopnWaves][256];
+    __shared__ int hsum[256];
     __shared__ int wsum[kTopnWaves];
+    __shared__ uint32_t alive_s[kAliveCap];  // key - kmin of the keys alive after pass 1
+    __shared__ int n_alive_s;
+    __shared__ uint32_t res_s[2];
     __shared__ uint32_t red_min[kTopnWaves], red_max[kTopnWaves];
 
     const int grp = blockIdx.x;
@@ -288,7 +284,6 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             red_min[wave] = lmin;
             red_max[wave] = lmax;
         }
-        if (tid < 256) hist[0][tid] = 0;
         __syncthreads();
         uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -300,24 +295,11 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         uint32_t prefix = 0;  // of key - kmin, above the current digit
         int krem = K;
         int shift = (range == 0u) ? 0 : 32 - __clz(static_cast<int>(range));
-        int pass = 0;
-        while (shift > 0) {
-            const int dbits = min(8, shift);
-            shift -= dbits;
-            const int hi = shift + dbits;
-            int* h = hist[pass % 3];
-#pragma unroll
-            for (int r = 0; r < KPT; ++r) {
-                if (base + r < NC) {
-                    const uint32_t kr = key[r] - kmin;
-                    const bool alive = hi >= 32 || ((kr >> hi) == (prefix >> hi));
-                    if (alive) atomicAdd(&h[(kr >> shift) & ((1u << dbits) - 1u)], 1);
-                }
-            }
-            if (tid < 256) hist[(pass + 1) % 3][tid] = 0;
-            __syncthreads();
-            // every wave finds the digit on its own: lane L covers digits
-            // 255-4L .. 252-4L (descending), counts are suffix sums
+        // digit search, by every wave on its own copy of the answer: lane L
+        // covers digits 255-4L .. 252-4L (descending), counts are suffix sums;
+        // returns the digit holding the krem-th largest alive key and how
+        // many alive keys lie in higher digits
+        auto find_digit = [&](const int* h, int& digit, int& above) __attribute__((always_inline)) {
             int c4[4], hv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) hv[i] = h[255 - 4 * lane - i];
@@ -336,11 +318,87 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             const int src = __ffsll(static_cast<unsigned long long>(bal)) - 1;  // exactly one lane
             const int my_digit = 255 - 4 * lane - (found_i < 0 ? 0 : found_i);
             const int my_above = excl + (found_i <= 0 ? 0 : c4[found_i - 1]);
-            const int digit = __shfl(my_digit, src, 64);
-            const int above = __shfl(my_above, src, 64);
+            digit = __builtin_amdgcn_readlane(my_digit, src);
+            above = __builtin_amdgcn_readlane(my_above, src);
+        };
+        // one radix pass over every key of the workgroup
+        auto block_pass = [&]() __attribute__((always_inline)) {
+            const int dbits = min(8, shift);
+            shift -= dbits;
+            const int hi = shift + dbits;
+            int* hw = hist[wave];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hw[lane + 64 * i] = 0;  // nobody reads it now
+#pragma unroll
+            for (int r = 0; r < KPT; ++r) {
+                if (base + r < NC) {
+                    const uint32_t kr = key[r] - kmin;
+                    const bool alive = hi >= 32 || ((kr >> hi) == (prefix >> hi));
+                    if (alive) atomicAdd(&hw[(kr >> shift) & ((1u << dbits) - 1u)], 1);
+                }
+            }
+            if (tid == 0) n_alive_s = 0;  // for the alive-key list below
+            __syncthreads();
+            if (tid < 256) {
+                int t = 0;
+#pragma unroll
+                for (int w = 0; w < kTopnWaves; ++w) t += hist[w][tid];
+                hsum[tid] = t;
+            }
+            __syncthreads();
+            int digit, above;
+            find_digit(hsum, digit, above);
             prefix |= static_cast<uint32_t>(digit) << shift;
             krem -= above;
-            ++pass;
+            return digit;
+        };
+
+        // The first pass runs over every key.  The keys still alive after it
+        // (those in the threshold's digit) are usually a few percent of them:
+        // they are gathered into LDS and the remaining passes run on that list
+        // in wave 0 alone, with no workgroup barriers.  A list too long for
+        // the buffer keeps to whole-workgroup passes.
+        if (shift > 0) {
+            const int d1 = block_pass();
+            const int n_alive = hsum[d1];
+            if (shift > 0 && n_alive <= kAliveCap) {
+#pragma unroll
+                for (int r = 0; r < KPT; ++r) {
+                    if (base + r < NC) {
+                        const uint32_t kr = key[r] - kmin;
+                        if ((kr >> shift) == (prefix >> shift)) alive_s[atomicAdd(&n_alive_s, 1)] = kr;
+                    }
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    while (shift > 0) {
+                        const int dbits = min(8, shift);
+                        shift -= dbits;
+                        const int hi = shift + dbits;
+                        int* hw = hist[0];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hw[lane + 64 * i] = 0;
+                        for (int i = lane; i < n_alive; i += kWave) {
+                            const uint32_t kr = alive_s[i];
+                            if ((kr >> hi) == (prefix >> hi))
+                                atomicAdd(&hw[(kr >> shift) & ((1u << dbits) - 1u)], 1);
+                        }
+                        int digit, above;
+                        find_digit(hw, digit, above);
+                        prefix |= static_cast<uint32_t>(digit) << shift;
+                        krem -= above;
+                    }
+                    if (lane == 0) {
+                        res_s[0] = prefix;
+                        res_s[1] = static_cast<uint32_t>(krem);
+                    }
+                }
+                __syncthreads();
+                prefix = res_s[0];
+                krem = static_cast<int>(res_s[1]);
+                shift = 0;
+            }
+            while (shift > 0) block_pass();
         }
         tau = kmin + prefix;
         need_eq = krem;
@@ -373,7 +431,8 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
                 take = eq_rank < need_eq;
                 ++eq_rank;
             }
-            if (take) out[pos++] = base + r;
+            if (take && pos < a.n_max) out[pos] = base + r;
+            pos += take ? 1 : 0;
         }
     }
     const int picked = (mode == 0) ? 0 : K;

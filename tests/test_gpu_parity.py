@@ -179,6 +179,38 @@ def test_select_decode_parity(case):
         assert eo <= 1e-4, eo  # fp32 I/O diagnostic bar
 
 
+def test_topn_long_row_of_ties():
+    """About 8000 candidates whose scores are almost all equal: the threshold
+    digit then holds thousands of keys after the first radix pass, which
+    exercises the whole-workgroup passes (the gathered-list path covers the
+    other cases).  Ties go to the lower block index on both sides."""
+    torch = _torch()
+    d, blk, Hq, Hkv = 64, 32, 4, 1
+    T = 8000 * blk + 17
+    L = bsa.Layout(1, Hq, Hkv, d, blk, (T + blk - 1) // blk + 1, BF16, MINMAX)
+    P = bsa.SelectParams(budget_tokens=0, sparsity_bp=9000, n_local=1, n_min=0)
+    P.n_max = bsa.block_count(P, L.max_blocks, blk)
+    rng = np.random.Generator(np.random.PCG64(123))
+    q = W.quantize(rng.standard_normal((1, Hq, d), dtype=np.float32), "bf16")
+    u = W.group_direction(q[0])
+    tmpl = rng.standard_normal((blk, d), dtype=np.float32)
+    K = np.tile(tmpl, ((T + blk - 1) // blk, 1))[:T].copy()
+    K[-17:] = rng.standard_normal((17, d), dtype=np.float32)
+    for j in (7, 1000, 4321, 7777, 7990):   # clearly above the tied mass
+        K[j * blk:(j + 1) * blk] += 3.0 * u
+    for j in (3, 2500, 6000):               # clearly below it
+        K[j * blk:(j + 1) * blk] -= 3.0 * u
+    K = W.quantize(K, "bf16")[None]
+    V = W.quantize(rng.standard_normal((1, T, d), dtype=np.float32), "bf16")
+    cache = bsa.allocate_cache(L, page_table=random_page_table(L, 8))
+    prefill(L, cache, [K], [V], [T])
+    idx, cnt, o, lse = run_select_decode(L, cache, to_dev(q, L), P)
+    ref = oracle_decode(P, q, [K], [V], [T], L)
+    compare_step(L, idx, cnt, o, lse, ref)
+    ridx = ref[(0, 0)][0]
+    assert {7, 1000, 4321, 7777, 7990} <= set(ridx.tolist())
+
+
 def test_dense_when_budget_covers_context():
     """Budget >= context: every block kept, equal to dense attention."""
     dtype, d, blk = BF16, 128, 64
