@@ -4,8 +4,11 @@ One step = the decode hot path for one generated token of every sequence,
 run for L distinct layer caches (default 8, so that the kept-block working
 set cannot stay resident in the 256 MB last-level cache):
   seq_lens += 1                          (shared by the layers)
-  per layer: bsa_build_block_desc (append the new k, v; update descriptors)
-             bsa_select_blocks     (score every non-local block, top-n)
+  per layer: bsa_append_select     (append the new k, v and update the
+                                   descriptors = bsa_build_block_desc, then
+                                   score every non-local block and keep the
+                                   top-n = bsa_select_blocks; the append rides
+                                   in the scoring launch)
              bsa_sparse_decode     (split-K attention over the kept blocks,
                                     log-sum-exp merge)
              bsa_rectify_chunk     (every f steps, workloads with rectification)
@@ -168,9 +171,10 @@ class Run:
         rect = bool(self.f) and self.steps_done % self.f == 0
         for l in range(self.layers):
             c = self.caches[l]
-            bsa.build_block_desc(self.L, c, inp["kn"][i, l], inp["vn"][i, l], 1)
-            # idx rows are n_max long (the buffer fits the largest n_max of the sweep)
-            bsa.select_blocks(self.L, c, inp["q"][i, l], P, self.idx[l], self.cnt[l], self.ws[l])
+            # append + select (the append shares the scoring launch); idx rows
+            # are n_max long (the buffer fits the largest n_max of the sweep)
+            bsa.append_select(self.L, c, inp["kn"][i, l], inp["vn"][i, l], inp["q"][i, l], P,
+                              self.idx[l], self.cnt[l], self.ws[l])
             if ev is not None:
                 ev[l][0].record()
             bsa.sparse_decode(self.L, c, inp["q"][i, l], self.idx[l], self.cnt[l], P.n_max,

@@ -21,8 +21,8 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 DESC_MINMAX, DESC_MEANPOOL = 0, 1
 OP_SELECT, OP_DECODE, OP_RECTIFY = 1, 2, 3
 
-EXPORTS = ("bsa_build_block_desc", "bsa_select_blocks", "bsa_sparse_decode",
-           "bsa_rectify_chunk", "bsa_workspace_size", "bsa_block_count",
+EXPORTS = ("bsa_build_block_desc", "bsa_select_blocks", "bsa_append_select",
+           "bsa_sparse_decode", "bsa_rectify_chunk", "bsa_workspace_size", "bsa_block_count",
            "bsa_status_string")
 
 
@@ -65,6 +65,7 @@ def lib():
     pl, pc, pp = ctypes.POINTER(c_layout), ctypes.POINTER(c_cache), ctypes.POINTER(c_select_params)
     L.bsa_build_block_desc.argtypes = [pl, pc, vp, vp, i32, vp, vp]
     L.bsa_select_blocks.argtypes = [pl, pc, vp, pp, vp, vp, vp, sz, vp]
+    L.bsa_append_select.argtypes = [pl, pc, vp, vp, vp, pp, vp, vp, vp, sz, vp]
     L.bsa_sparse_decode.argtypes = [pl, pc, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     L.bsa_rectify_chunk.argtypes = [pl, pc, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     L.bsa_workspace_size.argtypes = [pl, i32, i32]
@@ -210,6 +211,17 @@ def select_blocks(layout: Layout, cache: Cache, q, params: SelectParams, idx, cn
                                  ctypes.byref(params.c()), _ptr(idx), _ptr(cnt), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "bsa_select_blocks")
+
+
+def append_select(layout: Layout, cache: Cache, k_new, v_new, q, params: SelectParams, idx, cnt,
+                  ws, stream=None):
+    """build_block_desc (one token per sequence, k_new/v_new [B, Hkv, 1, d])
+    followed by select_blocks, with the append sharing the scoring launch."""
+    st = lib().bsa_append_select(ctypes.byref(layout.c()), ctypes.byref(cache.c()), _ptr(k_new),
+                                 _ptr(v_new), _ptr(q), ctypes.byref(params.c()), _ptr(idx),
+                                 _ptr(cnt), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream))
+    _check(st, "bsa_append_select")
 
 
 def sparse_decode(layout: Layout, cache: Cache, q, idx, cnt, n_max: int, softmax_scale: float,

@@ -187,6 +187,32 @@ bsa_status bsa_select_blocks(const bsa_layout* layout, const bsa_cache* cache, c
     return hip_status(launch_select(c, s, stream));
 }
 
+bsa_status bsa_append_select(const bsa_layout* layout, const bsa_cache* cache, const void* k_new,
+                             const void* v_new, const void* q, const bsa_select_params* params,
+                             int32_t* idx, int32_t* cnt, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    bsa_status st = check_layout(layout);
+    if (st != BSA_OK) return st;
+    if ((st = check_cache(cache)) != BSA_OK) return st;
+    if (!k_new || !v_new || !q || !idx || !cnt || !ws) return BSA_ERR_NULL;
+    if ((st = check_select_params(layout, params)) != BSA_OK) return st;
+    const CacheArgs c = make_args(layout, cache);
+    if (topn_keys_per_thread(c.max_blocks) == 0) return BSA_ERR_UNSUPPORTED;
+    if (ws_bytes < select_ws(c)) return BSA_ERR_WORKSPACE;
+    SelectArgs s;
+    s.q = q;
+    s.gate_w = params->gate_w;
+    s.budget_tokens = params->budget_tokens;
+    s.sparsity_bp = params->sparsity_bp;
+    s.n_local = params->n_local;
+    s.n_min = params->n_min;
+    s.n_max = params->n_max;
+    s.idx = idx;
+    s.cnt = cnt;
+    s.scores = static_cast<float*>(ws);
+    return hip_status(launch_append_select(c, k_new, v_new, s, stream));
+}
+
 bsa_status bsa_sparse_decode(const bsa_layout* layout, const bsa_cache* cache, const void* q,
                              const int32_t* idx, const int32_t* cnt, int32_t n_max,
                              float softmax_scale, void* o, float* lse, void* ws,

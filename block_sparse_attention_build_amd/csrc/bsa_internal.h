@@ -35,6 +35,10 @@ struct SelectArgs {
     float* scores;  // workspace [B*Hkv][score_stride(max_blocks)]
 };
 hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t stream);
+// Append of one token per sequence (kModeAppend, n_new = 1) and selection,
+// the append sharing the scoring launch.
+hipError_t launch_append_select(const CacheArgs& c, const void* k_new, const void* v_new,
+                                const SelectArgs& s, hipStream_t stream);
 // keys-per-thread bucket of the top-n kernel for a given max_blocks (0 = too many)
 int topn_keys_per_thread(int max_blocks);
 // row stride (floats) of the score workspace: max_blocks rounded up to 4

@@ -27,6 +27,7 @@
 //   appends the local blocks and pads with -1.
 #include "bsa_device.h"
 #include "bsa_internal.h"
+#include "kv_write_block.h"
 
 namespace bsa {
 
@@ -88,18 +89,18 @@ struct ScoreGeom {
     static constexpr int BPW = BPL * (kScoreThreads / kWave) * kScoreIters;  // blocks per WG
 };
 
+// Scores of the candidate blocks [bx * BPW, (bx + 1) * BPW) of group grp.
 template <int DT, int DESC, int D>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
+__device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int grp) {
     typedef typename Elem<DT>::T E;
     typedef ScoreGeom<DT, DESC, D> Gm;
     constexpr int EPL = Gm::EPL, LPB = Gm::LPB, BPL = Gm::BPL;
     constexpr int DE = (Gm::ES == 2) ? kBF16 : kF32;
     const CacheArgs& c = p.c;
     const SelectArgs& a = p.s;
-    const int grp = blockIdx.y;
     const int s = grp / c.Hkv;
     const int kvh = grp - s * c.Hkv;
-    const int c0 = blockIdx.x * Gm::BPW;
+    const int c0 = bx * Gm::BPW;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
@@ -207,6 +208,26 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
             out[j] = v;
         }
     }
+}
+
+template <int DT, int DESC, int D>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
+    score_block<DT, DESC, D>(p, static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y));
+}
+
+// Append of one token per sequence fused with the scoring: workgroups
+// x < score_gx score, the others write the new token and update the
+// descriptor of its block.  The two roles touch disjoint data -- the token
+// lands in the last block, which is local and never scored -- so they can
+// share one launch.
+template <int DT, int DESC, int D>
+__global__ __launch_bounds__(kScoreThreads) void append_score_kernel(ScoreParams sp, KvWriteParams kp,
+                                                                     int score_gx) {
+    const int bx = static_cast<int>(blockIdx.x);
+    if (bx < score_gx)
+        score_block<DT, DESC, D>(sp, bx, static_cast<int>(blockIdx.y));
+    else
+        kv_write_block<DT, DESC, kScoreThreads>(kp, bx - score_gx, static_cast<int>(blockIdx.y));
 }
 
 // ----------------------------- top-n ---------------------------------------
@@ -455,6 +476,23 @@ hipError_t launch_score_d(const ScoreParams& p, hipStream_t stream) {
     return p.c.d == 64 ? launch_score<DT, DESC, 64>(p, stream) : launch_score<DT, DESC, 128>(p, stream);
 }
 
+template <int DT, int DESC, int D>
+hipError_t launch_append_score(const ScoreParams& sp, const KvWriteParams& kp, hipStream_t stream) {
+    constexpr int BPW = ScoreGeom<DT, DESC, D>::BPW;
+    const int score_gx = (sp.c.max_blocks + BPW - 1) / BPW;
+    // one token per sequence touches one block
+    dim3 grid(score_gx + 1, sp.c.B * sp.c.Hkv);
+    hipLaunchKernelGGL((append_score_kernel<DT, DESC, D>), grid, dim3(kScoreThreads), 0, stream, sp, kp,
+                       score_gx);
+    return hipGetLastError();
+}
+
+template <int DT, int DESC>
+hipError_t launch_append_score_d(const ScoreParams& sp, const KvWriteParams& kp, hipStream_t stream) {
+    return sp.c.d == 64 ? launch_append_score<DT, DESC, 64>(sp, kp, stream)
+                        : launch_append_score<DT, DESC, 128>(sp, kp, stream);
+}
+
 template <int KPT>
 hipError_t launch_topn_k(const TopnParams& p, hipStream_t stream) {
     static_assert(KPT >= 4 || KPT == 1 || KPT == 2, "keys per thread");
@@ -472,16 +510,9 @@ int topn_keys_per_thread(int max_blocks) {
     return 0;
 }
 
-hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t stream) {
-    ScoreParams sp{c, s, score_stride(c.max_blocks)};
-    hipError_t err;
-    if (c.dtype == kBF16)
-        err = c.desc_kind == kMinMax ? launch_score_d<kBF16, kMinMax>(sp, stream)
-                                     : launch_score_d<kBF16, kMeanPool>(sp, stream);
-    else
-        err = c.desc_kind == kMinMax ? launch_score_d<kF32, kMinMax>(sp, stream)
-                                     : launch_score_d<kF32, kMeanPool>(sp, stream);
-    if (err != hipSuccess) return err;
+namespace {
+
+hipError_t launch_topn(const CacheArgs& c, const SelectArgs& s, hipStream_t stream) {
     TopnParams tp{c, s, score_stride(c.max_blocks)};
     switch (topn_keys_per_thread(c.max_blocks)) {
         case 1: return launch_topn_k<1>(tp, stream);
@@ -492,6 +523,36 @@ hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t st
         case 32: return launch_topn_k<32>(tp, stream);
         default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t stream) {
+    ScoreParams sp{c, s, score_stride(c.max_blocks)};
+    hipError_t err;
+    if (c.dtype == kBF16)
+        err = c.desc_kind == kMinMax ? launch_score_d<kBF16, kMinMax>(sp, stream)
+                                     : launch_score_d<kBF16, kMeanPool>(sp, stream);
+    else
+        err = c.desc_kind == kMinMax ? launch_score_d<kF32, kMinMax>(sp, stream)
+                                     : launch_score_d<kF32, kMeanPool>(sp, stream);
+    if (err != hipSuccess) return err;
+    return launch_topn(c, s, stream);
+}
+
+hipError_t launch_append_select(const CacheArgs& c, const void* k_new, const void* v_new,
+                                const SelectArgs& s, hipStream_t stream) {
+    ScoreParams sp{c, s, score_stride(c.max_blocks)};
+    KvWriteParams kp{c, kModeAppend, k_new, v_new, 1, nullptr};
+    hipError_t err;
+    if (c.dtype == kBF16)
+        err = c.desc_kind == kMinMax ? launch_append_score_d<kBF16, kMinMax>(sp, kp, stream)
+                                     : launch_append_score_d<kBF16, kMeanPool>(sp, kp, stream);
+    else
+        err = c.desc_kind == kMinMax ? launch_append_score_d<kF32, kMinMax>(sp, kp, stream)
+                                     : launch_append_score_d<kF32, kMeanPool>(sp, kp, stream);
+    if (err != hipSuccess) return err;
+    return launch_topn(c, s, stream);
 }
 
 }  // namespace bsa

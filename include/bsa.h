@@ -204,6 +204,23 @@ BSA_API bsa_status bsa_select_blocks(const bsa_layout* layout, const bsa_cache* 
                              size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * bsa_append_select -- the per-step pair bsa_build_block_desc (append mode,
+ * one token per sequence) then bsa_select_blocks, in two kernel launches
+ * instead of three: the new token lands in the last block, which is local
+ * and never scored, so writing it and scoring the other blocks run side by
+ * side in one launch.  Same references as the two calls it stands for.
+ * Results are identical to the two calls made in that order.
+ * k_new, v_new: [B][Hkv][1][d] in the KV dtype (the caller has already
+ *   advanced seq_lens by one).  Other arguments as in bsa_select_blocks.
+ * Errors: those of both calls.
+ * ------------------------------------------------------------------------- */
+BSA_API bsa_status bsa_append_select(const bsa_layout* layout, const bsa_cache* cache,
+                             const void* k_new, const void* v_new, const void* q,
+                             const bsa_select_params* params, int32_t* idx,
+                             int32_t* cnt, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * bsa_sparse_decode -- exact softmax attention of each query head over the
  * tokens of its group's kept blocks ("Rectified Sparse Attention ...",
  * Summary: group block-sparse attention; "Simple Attention Sparsification",

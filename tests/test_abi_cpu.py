@@ -20,9 +20,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["bsa_build_block_desc", "bsa_select_blocks", "bsa_sparse_decode",
-              "bsa_rectify_chunk", "bsa_workspace_size", "bsa_status_string",
-              "bsa_block_count"]:
+    for n in ["bsa_build_block_desc", "bsa_select_blocks", "bsa_append_select",
+              "bsa_sparse_decode", "bsa_rectify_chunk", "bsa_workspace_size",
+              "bsa_status_string", "bsa_block_count"]:
         assert n in names
     assert sorted(bsa.EXPORTS) == names
 
@@ -113,6 +113,23 @@ def test_select_null_and_workspace():
     assert _select(L_ok(), P, ws_bytes=16) == bsa.ERR_WORKSPACE
     # mean-pool descriptors need a gate weight
     assert _select(L_ok(desc_kind=bsa.DESC_MEANPOOL), P) == bsa.ERR_PARAM
+
+
+def test_append_select_validation():
+    L = L_ok()
+    C = bsa.c_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    p = ctypes.c_void_p(0x1000)
+    lib = bsa.lib()
+    P = bsa.SelectParams(sparsity_bp=9000, n_local=2, n_max=10)
+
+    def call(L=L, k=p, v=p, P=P, ws_bytes=1 << 30):
+        return lib.bsa_append_select(ctypes.byref(L.c()), ctypes.byref(C), k, v, p,
+                                     ctypes.byref(P.c()), p, p, p, ws_bytes, None)
+    assert call(k=None) == bsa.ERR_NULL
+    assert call(v=None) == bsa.ERR_NULL
+    assert call(P=bsa.SelectParams(sparsity_bp=9000, n_local=0, n_max=10)) == bsa.ERR_PARAM
+    assert call(ws_bytes=16) == bsa.ERR_WORKSPACE
+    assert call(L=L_ok(d=96)) == bsa.ERR_UNSUPPORTED
 
 
 def test_decode_and_rectify_validation():

@@ -179,6 +179,54 @@ def test_select_decode_parity(case):
         assert eo <= 1e-4, eo  # fp32 I/O diagnostic bar
 
 
+@pytest.mark.parametrize("dtype,d,blk,kind", [(BF16, 128, 64, MINMAX), (BF16, 64, 128, MEAN),
+                                              (F32, 64, 32, MINMAX)])
+def test_append_select_equals_the_two_calls(dtype, d, blk, kind):
+    """bsa_append_select gives the cache, descriptors, idx and cnt of
+    bsa_build_block_desc (one token) followed by bsa_select_blocks, over
+    several steps that open and fill blocks."""
+    torch = _torch()
+    lengths = [blk * 9 - 2, blk * 5 + 3]
+    Hq, Hkv = 8, 2
+    B = len(lengths)
+    max_blocks = (max(lengths) + 8 + blk - 1) // blk + 1
+    L = bsa.Layout(B, Hq, Hkv, d, blk, max_blocks, dtype, kind)
+    P = bsa.SelectParams(budget_tokens=0, sparsity_bp=8000, n_local=1, n_min=2)
+    P.n_max = bsa.block_count(P, max_blocks, blk)
+    q, Ks, Vs, Wg = make_inputs(77, B, Hq, Hkv, d, [T + 8 for T in lengths], dtype, kind)
+    if Wg is not None:
+        P.gate_w = to_dev(Wg, bsa.Layout(1, 1, 1, d, blk, 1, BF16))
+    caches = []
+    for _ in range(2):
+        c = bsa.allocate_cache(L, page_table=random_page_table(L, 3))
+        c.k_pool.zero_()
+        c.v_pool.zero_()
+        c.desc.zero_()
+        prefill(L, c, Ks, Vs, lengths)
+        caches.append(c)
+    ws = torch.empty(bsa.workspace_size(L, bsa.OP_SELECT, P.n_max), dtype=torch.uint8, device="cuda")
+    q_dev = to_dev(q, L)
+    for step in range(8):
+        kn = to_dev(np.stack([Ks[s][:, lengths[s] + step] for s in range(B)])[:, :, None], L)
+        vn = to_dev(np.stack([Vs[s][:, lengths[s] + step] for s in range(B)])[:, :, None], L)
+        out = []
+        for which, c in enumerate(caches):
+            c.seq_lens += 1
+            idx = torch.full((B, Hkv, P.n_max), -7, dtype=torch.int32, device="cuda")
+            cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device="cuda")
+            if which == 0:
+                bsa.build_block_desc(L, c, kn, vn, 1)
+                bsa.select_blocks(L, c, q_dev, P, idx, cnt, ws)
+            else:
+                bsa.append_select(L, c, kn, vn, q_dev, P, idx, cnt, ws)
+            torch.cuda.synchronize()
+            out.append((idx.clone(), cnt.clone()))
+        assert torch.equal(out[0][0], out[1][0]) and torch.equal(out[0][1], out[1][1]), step
+        assert torch.equal(caches[0].k_pool, caches[1].k_pool)
+        assert torch.equal(caches[0].v_pool, caches[1].v_pool)
+        assert torch.equal(caches[0].desc, caches[1].desc)
+
+
 def test_topn_long_row_of_ties():
     """About 8000 candidates whose scores are almost all equal: the threshold
     digit then holds thousands of keys after the first radix pass, which
