@@ -122,10 +122,31 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
         const int j = min(c0 + (it * (kScoreThreads / kWave) + wave) * BPL + bl, c.max_blocks - 1);
         Chunk<DE>::load(base + static_cast<int64_t>(j) * Gm::BR, x[it]);
     }
-    // 2. the group's queries go through LDS in one parallel round trip
-    __shared__ float qs[16 * D];
+    // 2. the group's query weights, once per workgroup, into LDS:
+    //    min/max: Q-_i = sum_h min(q_hi, 0) (pairs with the min row) and
+    //             Q+_i = sum_h max(q_hi, 0) (pairs with the max row);
+    //    mean-pool: u_i = sum_h q_hi, then w = W u.
+    //    (heads summed in order h = 0..G-1)
+    __shared__ float qw[2 * D];
     const E* qg = static_cast<const E*>(a.q) + (static_cast<int64_t>(s) * c.Hq + kvh * c.G) * D;
-    for (int i = tid; i < c.G * D; i += kScoreThreads) qs[i] = Elem<DT>::load(qg, i);
+    if (DESC == kMinMax) {
+        if (tid < 2 * D) {
+            const int i = tid % D;
+            const bool upper = tid >= D;
+            float acc = 0.f;
+            for (int h = 0; h < c.G; ++h) {
+                const float xq = Elem<DT>::load(qg, h * D + i);
+                acc += upper ? fmaxf(xq, 0.f) : fminf(xq, 0.f);
+            }
+            qw[tid] = acc;
+        }
+    } else {
+        if (tid < D) {
+            float acc = 0.f;
+            for (int h = 0; h < c.G; ++h) acc += Elem<DT>::load(qg, h * D + tid);
+            qw[tid] = acc;
+        }
+    }
     const int T = c.seq_lens[s];
     const int NB = (T + c.block - 1) / c.block;
     const int nl = min(a.n_local, NB);
@@ -134,31 +155,19 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
     if (c0 >= NC) return;  // uniform across the workgroup
     float wv[EPL];
     if (DESC == kMinMax) {
+        const float* src = qw + (max_row ? D : 0) + ch0;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            float acc = 0.f;
-            for (int h = 0; h < c.G; ++h) {
-                const float xq = qs[h * D + ch0 + e];
-                acc += max_row ? fmaxf(xq, 0.f) : fminf(xq, 0.f);
-            }
-            wv[e] = acc;
-        }
+        for (int e = 0; e < EPL; ++e) wv[e] = src[e];
     } else {
-        // u = sum_h q_h, then w = W u, both in LDS: kScoreThreads / D threads
-        // per output channel, each a 16-byte-load dot product over its share
-        // of the row, then the shares added in fixed order
+        // w = W u in LDS: kScoreThreads / D threads per output channel, each
+        // a 16-byte-load dot product over its share of the row, then the
+        // shares added in fixed order
         constexpr int PARTS = kScoreThreads / D;
         constexpr int KP = D / PARTS;
         static_assert(PARTS * D == kScoreThreads && KP % 8 == 0, "gate matvec split");
-        __shared__ float u_s[D];
+        const float* u_s = qw;
         __shared__ float w_part[kScoreThreads];
         __shared__ float w_s[D];
-        for (int i = tid; i < D; i += kScoreThreads) {
-            float acc = 0.f;
-            for (int h = 0; h < c.G; ++h) acc += qs[h * D + i];
-            u_s[i] = acc;
-        }
-        __syncthreads();
         {
             const int r = tid % D;
             const int part = tid / D;
