@@ -28,9 +28,11 @@ value = effective HBM GB/s of the graph-timed step:
   amortised, where the workload rectifies).
 """
 import argparse
+import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -41,6 +43,31 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix, published
 METRIC = "sparse decode us/step/layer + effective HBM GB/s (% of peak) at 64K-512K ctx"
+
+
+# HBM traffic of one bsa_sparse_decode call, from the committed rocprofv3
+# counter runs (FETCH_SIZE, WRITE_SIZE, calibrated on a plain copy); reported
+# only while the decode sources are the ones the counters were taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sparse_decode_long_512k_p90_traffic.md")
+TRAFFIC_SOURCES = ("block_sparse_attention_build_amd/csrc/decode.hip",
+                   "block_sparse_attention_build_amd/csrc/bsa_device.h")
+
+
+def measured_traffic(workload, bp):
+    if workload != "long_512k" or bp != 9000:
+        return None
+    try:
+        txt = open(TRAFFIC_FILE).read()
+        h = hashlib.sha256()
+        for f in TRAFFIC_SOURCES:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+    except OSError:
+        return None
+    t = re.search(r"traffic_bytes_per_launch:\s*(\d+)", txt)
+    src = re.search(r"sources sha256[^:]*:\s*([0-9a-f]{64})", txt)
+    if not t or not src or src.group(1) != h.hexdigest():
+        return None
+    return int(t.group(1))
 
 
 def parse():
@@ -409,12 +436,13 @@ def main():
         "bytes": {"effective_per_step_layer": head["bytes_per_step_layer"],
                   "descriptor_per_step_layer": int(m0["graph"]["desc_bytes"]),
                   "kept_kv_per_step_layer": int(m0["graph"]["kv_bytes"])},
-        "roofline": {"kernel": "decode_bf16_kernel + combine (bsa_sparse_decode)",
+        "roofline": {"kernel": "bsa_sparse_decode (decode_bf16_kernel + combine_kernel)",
                      "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBS, 4),
                      "avg_launch_us": round(m0["decode_us_avg"], 3),
                      "algorithmic_bytes_per_launch": int(m0["decode_kv_bytes_per_call"]),
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name, bp0),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE)"},
         "eager_us_per_step_layer": head["eager_us_per_step_layer"],
         "workloads": [head] + [summarize(w, bp, args.layers, m)[1] for bp, m in results[1:]],
     }
