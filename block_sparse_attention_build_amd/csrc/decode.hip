@@ -35,22 +35,28 @@ namespace bsa {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
-
-// Tuning: waves per SIMD the bf16 kernel is register-limited to, and the
-// number of workgroups a decode call aims for (one resident round on 256 CUs).
+// Tuning: threads per workgroup, waves per SIMD the bf16 kernel is
+// register-limited to, and the number of workgroups a decode call aims for
+// (one resident round on 256 CUs).
 #ifndef BSA_DECODE_WAVES_PER_EU
 #define BSA_DECODE_WAVES_PER_EU 2
 #endif
 #ifndef BSA_DECODE_TARGET_WGS
-#define BSA_DECODE_TARGET_WGS 512
+#define BSA_DECODE_TARGET_WGS 256
 #endif
+#ifndef BSA_DECODE_UNIT_LDS
+#define BSA_DECODE_UNIT_LDS (112 * 1024)  // LDS bytes for the per-unit partials
+#endif
+constexpr int kThreads = 256;     // fp32 kernel
+constexpr int kWaves = kThreads / kWave;
+constexpr int kDecThreads = 512;  // bf16 kernel: 8 waves
 
 struct DecodeParams {
     CacheArgs c;
     DecodeArgs a;
     int max_blocks_per_wg;  // LDS slots for a split's block/page ids
+    int unit_tiles;         // bf16: tiles per unit of work
+    int max_units;          // bf16: LDS slots for unit partials
 };
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
@@ -88,19 +94,30 @@ __device__ __forceinline__ void merge_waves_and_store(const float* sm, const flo
     }
 }
 
+// The bf16 kernel: one workgroup of kDecThreads (8 waves) per (sequence, KV
+// head, split), one workgroup per CU.  The split's kept tiles are cut into
+// units of unit_tiles tiles; waves claim units one at a time from an LDS
+// counter, so a wave that the hardware serves faster simply takes more units
+// and all waves finish together.  Each unit leaves its own partial
+// (running max, sum, unnormalised O) in LDS, and the units are merged in
+// unit order at the end, so the result does not depend on which wave took
+// which unit.
 template <int D, int BLK>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kDecThreads)
 __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf16_kernel(
     DecodeParams p) {
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int NT = D / 16;   // column tiles of the PV product
     constexpr int TPB = BLK / 32;
     extern __shared__ float smem[];
-    float* sm = smem;                    // [kWaves][16]
-    float* sl = sm + kWaves * 16;        // [kWaves][16]
-    float* so = sl + kWaves * 16;        // [kWaves][G][D]
-    int* s_blk = reinterpret_cast<int*>(so + kWaves * p.c.G * D);  // [max_blocks_per_wg]
-    int* s_page = s_blk + p.max_blocks_per_wg;                      // [max_blocks_per_wg]
+    const int MU = p.max_units;
+    const int G = p.c.G;
+    float* um = smem;                    // [MU][16] running max per unit and head column
+    float* ul = um + MU * 16;            // [MU][16] running sum
+    float* uo = ul + MU * 16;            // [MU][G][D] unnormalised O
+    int* s_blk = reinterpret_cast<int*>(uo + MU * G * D);  // [max_blocks_per_wg]
+    int* s_page = s_blk + p.max_blocks_per_wg;              // [max_blocks_per_wg]
+    __shared__ int s_next;
 
     const CacheArgs& c = p.c;
     const DecodeArgs& a = p.a;
@@ -108,15 +125,13 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     const int grp = blockIdx.y;
     const int s = grp / c.Hkv;
     const int kvh = grp - s * c.Hkv;
-    const int G = c.G;
     const int S = a.splits;
     // The split ranges cover n_max blocks (known before any load), so the
     // block ids, the kept count, the length and the queries are requested
-    // together; entries at or past cnt are empty tiles.
+    // together.
     const int U = a.n_max * TPB;
     const int u0 = static_cast<int>(static_cast<int64_t>(U) * split / S);
     const int u1 = static_cast<int>(static_cast<int64_t>(U) * (split + 1) / S);
-    const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int g = lane >> 4;
     const int col = lane & 15;
@@ -142,13 +157,19 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     const int nblk = (u1 > u0) ? (u1 - 1) / TPB - pb0 + 1 : 0;
     const int cnt = a.cnt[grp];
     const int T = c.seq_lens[s];
-    for (int i = threadIdx.x; i < nblk; i += kThreads) {
+    for (int i = threadIdx.x; i < nblk; i += kDecThreads) {
         const int blk = idxrow[pb0 + i];
         const bool kept = pb0 + i < cnt;
-        s_blk[i] = kept ? blk : (T / BLK + 1);  // an empty tile: starts past T
+        s_blk[i] = kept ? blk : 0;
         s_page[i] = kept ? ptrow[blk] : 0;
     }
+    if (threadIdx.x == 0) s_next = 0;
     __syncthreads();
+
+    // the kept tiles of the split, in units
+    const int uend = min(u1, cnt * TPB);
+    const int UT = p.unit_tiles;
+    const int n_units = (uend > u0) ? (uend - u0 + UT - 1) / UT : 0;
 
     floatx4 oacc[NT];
 #pragma unroll
@@ -159,21 +180,14 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     const uint16_t* kpool = static_cast<const uint16_t*>(c.k_pool);
     const uint16_t* vpool = static_cast<const uint16_t*>(c.v_pool);
     const float sl2 = a.scale_log2;
-
-    // This wave's tiles: a contiguous, balanced share of the split, clipped
-    // to the kept count.  The loop is software-pipelined: the next tile's K
-    // loads are issued as soon as QK has consumed the current K registers,
-    // and its V loads as soon as PV has consumed V.  The steady-state body
-    // has no branch around a load (the last tile is a separate copy without
-    // next-tile loads; tiles past the end of a partial block are loaded and
-    // fully masked), so the compiler's wait counters only wait for the
-    // registers each step needs.  Tile addressing is wave-uniform.
-    const int per = u1 - u0;
-    const int w0 = u0 + per * wave / kWaves;
-    const int w1 = min(u0 + per * (wave + 1) / kWaves, cnt * TPB);
     const uint16_t* kl = kpool + lane * 8;
     const uint16_t* vl = vpool + lane * 8;
     u32x4 kr[2 * KS], vr[NT];
+    auto grab = [&]() __attribute__((always_inline)) {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(&s_next, 1);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
     // tile u -> (element offset of its 32-token run, tokens valid in it)
     auto resolve = [&](int u, int64_t& off, int& nvalid) __attribute__((always_inline)) {
         const int pi = u / TPB;
@@ -191,7 +205,7 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
 #pragma unroll
         for (int n = 0; n < NT; ++n) vr[n] = ldg16(vl + off + n * 512);
     };
-    // one tile: QK, online softmax, PV; NEXT: also issue tile u+1's loads
+    // one tile: QK, online softmax, PV; NEXT: also issue the next tile's loads
     auto step = [&](const int nvalid, const bool next, const int64_t off_nxt)
                     __attribute__((always_inline)) {
         floatx4 sacc[2];
@@ -216,7 +230,7 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         if (__ballot(tmax > m_run) != 0) {  // some head's running max grows
             const float m_new = fmaxf(m_run, tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 on the first tile
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
             m_run = m_new;
             // O rows are heads 4g+e; their alpha lives in lane 4g+e
@@ -257,40 +271,91 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
         }
         if (next) load_v(off_nxt);
     };
-    if (w0 < w1) {
+    // the finished unit's partial to LDS, and a fresh state
+    auto flush = [&](int unit) __attribute__((always_inline)) {
+        float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+        l_tot += __shfl_xor(l_tot, 32, 64);
+        if (g == 0) {
+            um[unit * 16 + col] = m_run;
+            ul[unit * 16 + col] = l_tot;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int h = 4 * g + e;
+            if (h < G) {
+#pragma unroll
+                for (int n = 0; n < NT; ++n) uo[(unit * G + h) * D + n * 16 + col] = oacc[n][e];
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NT; ++n) oacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+        m_run = -INFINITY;
+        l_run = 0.f;
+    };
+
+    // Tile loop, software-pipelined across unit boundaries: the next tile's
+    // K loads are issued as soon as QK has consumed the current K registers
+    // and its V loads as soon as PV has consumed V; the next unit is claimed
+    // while the last tile of the current one is being computed.  Every load
+    // in the steady-state body is unconditional (the last tile is a separate
+    // call without next-tile loads), so the compiler's wait counters only
+    // wait for the registers each step needs.  Tile addressing is
+    // wave-uniform.
+    int unit = grab();
+    if (unit < n_units) {
+        int t = u0 + unit * UT;
+        int t_end = min(t + UT, uend);
         int64_t off = 0;
         int nv = 0;
-        resolve(w0, off, nv);
+        resolve(t, off, nv);
         load_k(off);
         load_v(off);
-        for (int u = w0; u + 1 < w1; ++u) {
+        while (true) {
+            int nt = t + 1, nunit = unit, nend = t_end;
+            if (nt >= t_end) {  // last tile of the unit: claim the next one
+                nunit = grab();
+                nt = u0 + nunit * UT;
+                nend = min(nt + UT, uend);
+            }
+            if (nunit >= n_units) break;
             int64_t off_nxt = 0;
             int nv_nxt = 0;
-            resolve(u + 1, off_nxt, nv_nxt);
+            resolve(nt, off_nxt, nv_nxt);
             step(nv, true, off_nxt);
+            if (nunit != unit) flush(unit);
+            unit = nunit;
+            t = nt;
+            t_end = nend;
             nv = nv_nxt;
         }
         step(nv, false, 0);
-    }
-
-    // per-wave totals: l summed over the 4 lane groups of each head column
-    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
-    if (g == 0) {
-        sm[wave * 16 + col] = m_run;
-        sl[wave * 16 + col] = l_tot;
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const int h = 4 * g + e;
-        if (h < G) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) so[(wave * G + h) * D + n * 16 + col] = oacc[n][e];
-        }
+        flush(unit);
     }
     __syncthreads();
-    merge_waves_and_store(sm, sl, so, G, D, a.o_part, a.lse_part,
-                          static_cast<int64_t>(s) * c.Hq + kvh * G, S, split);
+
+    // merge of the units, in unit order, into one partial per head
+    const int64_t head_row0 = static_cast<int64_t>(s) * c.Hq + kvh * G;
+    for (int k = threadIdx.x; k < G * D; k += kDecThreads) {
+        const int h = k / D;
+        const int ch = k - h * D;
+        float M = -INFINITY;
+        for (int u = 0; u < n_units; ++u) M = fmaxf(M, um[u * 16 + h]);
+        const int64_t row = head_row0 + h;
+        float* op = a.o_part + (row * S + split) * D;
+        if (M == -INFINITY) {
+            op[ch] = 0.f;
+            if (ch == 0) a.lse_part[row * S + split] = -INFINITY;
+            continue;
+        }
+        float L = 0.f, acc = 0.f;
+        for (int u = 0; u < n_units; ++u) {
+            const float sc = exp2f(um[u * 16 + h] - M);
+            L += ul[u * 16 + h] * sc;
+            acc += uo[(u * G + h) * D + ch] * sc;
+        }
+        op[ch] = acc / L;
+        if (ch == 0) a.lse_part[row * S + split] = M + log2f(L);
+    }
 }
 
 // fp32 caches: same split, plain arithmetic.  Lane t < 32 owns token t of a
@@ -484,11 +549,20 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 }
 
 template <int D, int BLK>
-hipError_t launch_bf16(const DecodeParams& p, hipStream_t stream) {
-    const size_t shm = sizeof(float) * (2 * kWaves * 16 + kWaves * p.c.G * D) +
+hipError_t launch_bf16(DecodeParams p, hipStream_t stream) {
+    // units: as many LDS partial slots as the budget holds, each unit at
+    // least two tiles; the split's tiles / units tiles per unit
+    const int tiles = (p.a.n_max * (BLK / 32) + p.a.splits - 1) / p.a.splits;
+    const int unit_bytes = static_cast<int>(sizeof(float)) * (32 + p.c.G * D);
+    const int slots = BSA_DECODE_UNIT_LDS / unit_bytes;
+    int ut = (tiles + slots - 1) / slots;
+    if (ut < 2) ut = 2;
+    p.unit_tiles = ut;
+    p.max_units = (tiles + ut - 1) / ut;
+    const size_t shm = static_cast<size_t>(unit_bytes) * p.max_units +
                        2 * sizeof(int) * p.max_blocks_per_wg;
     dim3 grid(p.a.splits, p.c.B * p.c.Hkv);
-    hipLaunchKernelGGL((decode_bf16_kernel<D, BLK>), grid, dim3(kThreads), shm, stream, p);
+    hipLaunchKernelGGL((decode_bf16_kernel<D, BLK>), grid, dim3(kDecThreads), shm, stream, p);
     return hipGetLastError();
 }
 
@@ -514,8 +588,8 @@ hipError_t launch_f32(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 int decode_splits(const CacheArgs& c, int n_max) {
-    // about BSA_DECODE_TARGET_WGS workgroups over the chip, at least 4 tiles
-    // (one per wave) in every split.
+    // about BSA_DECODE_TARGET_WGS workgroups over the chip (one per CU for
+    // the bf16 kernel), at least 4 tiles in every split.
     const int groups = c.B * c.Hkv;
     const int tiles = n_max * (c.block / 32);
     int S = (BSA_DECODE_TARGET_WGS + groups - 1) / groups;
@@ -553,7 +627,7 @@ hipError_t launch_decode(const CacheArgs& c, const DecodeArgs& a, hipStream_t st
     // that many / TPB + 1 blocks (+1 more when it starts inside a block)
     const int tpb = c.block / 32;
     const int tiles = (a.n_max * tpb + a.splits - 1) / a.splits;
-    DecodeParams p{c, a, tiles / tpb + 2};
+    DecodeParams p{c, a, tiles / tpb + 2, 0, 0};
     hipError_t err;
     if (c.dtype == kBF16)
         err = c.d == 64 ? launch_bf16_d<64>(p, stream) : launch_bf16_d<128>(p, stream);
