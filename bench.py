@@ -82,6 +82,9 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=40)
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads (sparsity sweep, 32K, batched, ReSA loop)")
+    ap.add_argument("--resa-sweep", action="store_true",
+                    help="also run the ragged ReSA loop over f in {16,32,64,128} x p in "
+                         "{0.9,0.95,0.98} and compare its bytes with 1/b + (1-p) + 1/f")
     return ap.parse_args()
 
 
@@ -477,7 +480,38 @@ def main():
             print(f"# {name}: {time.time() - t0:.1f}s {json.dumps(mx)}", file=sys.stderr, flush=True)
             del rx
             torch.cuda.empty_cache()
+    if args.resa_sweep:
+        out["resa_sweep"] = resa_sweep(args, dev)
     print(json.dumps(out), flush=True)
+
+
+def resa_sweep(args, dev):
+    """The ragged ReSA loop over the rectify interval f and the sparsity p:
+    amortised step time and bytes per step against the dense read of the
+    whole cache, next to the cost model 1/b + (1 - p) + 1/f."""
+    import torch
+
+    import workloads as W
+    rows = []
+    for f in (16, 32, 64, 128):
+        for bp in (9000, 9500, 9800):
+            w = W.get("resa_ragged", rectify_f=f, sparsity_bp=bp)
+            run = Run(w, args.layers, dev)
+            m = measure(run, max(args.steps, 2 * f), args.warmup)
+            gm = m["graph"]
+            dense = sum(T * w.Hkv * 2 * w.d * 2 for T in w.T0)
+            rows.append({"f": f, "sparsity_bp": bp,
+                         "us_per_step_layer": round(gm["us_per_step_layer"], 2),
+                         "bytes_per_step_layer": int(gm["eff_bytes_per_step_layer"]),
+                         "bytes_over_dense": round(gm["eff_bytes_per_step_layer"] / dense, 4),
+                         "model_1/b+(1-p)+1/f": round(1 / w.block + (10000 - bp) / 10000 + 1 / f, 4),
+                         "effective_GBps": round(gm["eff_bytes_per_step_layer"] /
+                                                 (gm["us_per_step_layer"] * 1e-6) / 1e9, 1),
+                         "rectify_us_per_call": round(m["rectify"]["us_avg"], 1) if "rectify" in m else None})
+            print(f"# resa sweep {rows[-1]}", file=sys.stderr, flush=True)
+            del run
+            torch.cuda.empty_cache()
+    return rows
 
 
 if __name__ == "__main__":

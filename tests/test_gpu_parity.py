@@ -344,20 +344,22 @@ def test_tiny_fp32_decode_loop():
 # Rectification
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,d,blk,f,lengths", [
-    (BF16, 128, 64, 32, [300, 517]),
-    (BF16, 128, 64, 16, [2100]),
-    (BF16, 128, 128, 64, [4500, 200, 64]),
-    (BF16, 64, 64, 1, [129]),
-    (F32, 64, 64, 32, [300, 97]),
-    (BF16, 128, 32, 33, [1000]),
+@pytest.mark.parametrize("dtype,d,blk,f,lengths,Hq,Hkv", [
+    (BF16, 128, 64, 32, [300, 517], 8, 2),
+    (BF16, 128, 64, 16, [2100], 8, 2),
+    (BF16, 128, 128, 64, [4500, 200, 64], 8, 2),
+    (BF16, 64, 64, 1, [129], 8, 2),
+    (F32, 64, 64, 32, [300, 97], 8, 2),
+    (BF16, 128, 32, 33, [1000], 8, 2),
+    (BF16, 128, 64, 128, [3000, 700], 8, 2),   # 512 rows per KV head: two row groups
+    (BF16, 64, 64, 20, [1500], 16, 1),         # G = 16: 320 rows, a partial second group
+    (BF16, 128, 64, 16, [900, 1300], 2, 2),    # G = 1: 16 rows (the 4-wave shape)
 ])
-def test_rectify_parity(dtype, d, blk, f, lengths):
+def test_rectify_parity(dtype, d, blk, f, lengths, Hq, Hkv):
     """Overwrite + descriptor refresh + causal dense attention of the f
     queries, against the oracle (all rows)."""
     torch = _torch()
     B = len(lengths)
-    Hq, Hkv = 8, 2
     G = Hq // Hkv
     max_blocks = (max(lengths) + blk - 1) // blk + 1
     L = bsa.Layout(B, Hq, Hkv, d, blk, max_blocks, dtype, MINMAX)
