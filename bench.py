@@ -53,6 +53,13 @@ TRAFFIC_SOURCES = ("block_sparse_attention_build_amd/csrc/decode.hip",
                    "block_sparse_attention_build_amd/csrc/bsa_device.h")
 
 
+def code_only(src):
+    """Source text without // comments and blank lines (comment edits do not
+    change the kernel the counters were taken on)."""
+    lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in src.splitlines())
+    return "\n".join(ln for ln in lines if ln).encode()
+
+
 def measured_traffic(workload, bp):
     if workload != "long_512k" or bp != 9000:
         return None
@@ -60,7 +67,7 @@ def measured_traffic(workload, bp):
         txt = open(TRAFFIC_FILE).read()
         h = hashlib.sha256()
         for f in TRAFFIC_SOURCES:
-            h.update(open(os.path.join(ROOT, f), "rb").read())
+            h.update(code_only(open(os.path.join(ROOT, f)).read()))
     except OSError:
         return None
     t = re.search(r"traffic_bytes_per_launch:\s*(\d+)", txt)

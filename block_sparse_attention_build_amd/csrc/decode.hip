@@ -8,9 +8,10 @@
 // Flash-Decoding (cited in the ReSA page's references): split the keys,
 // merge the partial (o, lse) pairs.
 //
-// bf16 path (the bandwidth-critical kernel).  One workgroup = 4 waves =
-// one (sequence, KV head, split); the split is a contiguous range of 32-token
-// tiles of the group's kept-block list, and the waves take every 4th tile.
+// bf16 path (the bandwidth-critical kernel).  One workgroup = 8 waves = one
+// (sequence, KV head, split), one workgroup per CU; the split is a contiguous
+// range of 32-token tiles of the group's kept-block list, cut into units of
+// unit_tiles tiles that the waves claim from an LDS counter.
 // Per tile a wave issues 16-byte loads of 8 KiB of K and 8 KiB of V (d=128):
 // every load instruction reads one contiguous KiB because the page layout
 // stores each KiB as one matrix-core operand.  The wave then computes
@@ -21,8 +22,9 @@
 // where P is exactly the S^T accumulator the lane already holds (the V page
 // layout orders tokens to match), split into bf16 hi + lo parts so that the
 // weights keep ~16 mantissa bits.  K and V are read once per group, never
-// once per head.  At the end the 4 waves merge through LDS and the
-// workgroup writes one normalised partial (o, base-2 lse) per head.
+// once per head.  Each unit leaves a partial (max, sum, O) in LDS; the units
+// are merged in unit order and the workgroup writes one normalised partial
+// (o, base-2 lse) per head, which the merge kernel combines across splits.
 //
 // fp32 path.  Same split structure, plain VALU arithmetic (no fp32 matrix
 // operand layout is defined for the pages); used by the small fp32 cases.

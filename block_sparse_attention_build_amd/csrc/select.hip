@@ -17,14 +17,20 @@
 //   Q-_i = sum_h min(q_hi, 0)  -- one 2d-long dot product per block instead
 //   of G of them.  Mean-pool score: (W sum_h q_h) . sum_j / tokens_j.
 //   Scores are fp32.  Each block's descriptor row is read by a run of lanes
-//   with 16-byte loads and reduced with cross-lane adds.
+//   with 16-byte loads and reduced with DPP row adds; the group's query
+//   weights are formed once per workgroup in LDS.  A variant also carries
+//   the decode step's append (one extra workgroup per group, see
+//   append_score_kernel).
 // Kernel 2 (top-n): one 1024-thread workgroup per group holds the candidate
-//   scores in registers as order-preserving uint32 keys, finds the n-th
-//   largest key with an MSB-first radix select over LDS histograms (digits
-//   taken from key - min_key so that the first digit already spreads the
-//   keys), then compacts the kept blocks in ascending index order with two
-//   block-wide prefix scans (ties at the threshold go to the lower index),
-//   appends the local blocks and pads with -1.
+//   scores in registers as order-preserving uint32 keys and finds the n-th
+//   largest key with an MSB-first radix select (digits taken from
+//   key - min_key so that the first digit already spreads the keys): the
+//   first pass histograms every key (per-wave LDS histograms), the keys left
+//   in the threshold's digit are gathered into an LDS list and wave 0
+//   finishes the search on it.  The kept blocks are then compacted in
+//   ascending index order with one block-wide prefix scan (ties at the
+//   threshold go to the lower index), the local blocks appended and the row
+//   padded with -1.
 #include "bsa_device.h"
 #include "bsa_internal.h"
 #include "kv_write_block.h"
