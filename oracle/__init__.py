@@ -54,6 +54,15 @@ def lib():
                                    ctypes.c_double, _i32p, _i64, _f64p, _f64p,
                                    _f64p]
     L.orc_decode_group.restype = _i64
+    L.orc_gate_bias.argtypes = [_f64p, _i64, _int, ctypes.c_double, _i32p, _i64,
+                                _f64p]
+    L.orc_attend_biased.argtypes = [_f32p, _f32p, _f32p, _i64, _int, _int, _i32p,
+                                    _i64, _f64p, ctypes.c_double, _f64p, _f64p]
+    L.orc_decode_group_gated.argtypes = [_f32p, _int, _f32p, _f32p, _i64, _int,
+                                         _int, _int, _f32p, _i64, _int, _int, _int,
+                                         ctypes.c_double, ctypes.c_double, _i32p,
+                                         _i64, _f64p, _f64p, _f64p]
+    L.orc_decode_group_gated.restype = _i64
     _LIB = L
     return L
 
@@ -205,3 +214,63 @@ def decode_group(q, K, V, b, desc_kind, W=None, budget_tokens=0, sparsity_bp=0,
     if want_scores:
         out = out + (s,)
     return out
+
+
+def gate_bias(scores, NB, n_local, tau, idx):
+    """Log-gate bias (SAS) of the selected blocks idx: log softmax(tau * s)
+    over the NB - n_local candidates, 0 for the local blocks.
+    scores: [>= NB - n_local] candidate scores."""
+    full = np.full(max(NB, 1), np.nan, np.float64)
+    sc = np.asarray(scores, np.float64)
+    full[: min(sc.shape[0], NB)] = sc[: NB]
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    bias = np.empty(max(idx.shape[0], 1), np.float64)
+    lib().orc_gate_bias(full.ctypes.data_as(_f64p), NB, n_local, tau,
+                        idx.ctypes.data_as(_i32p), idx.shape[0],
+                        bias.ctypes.data_as(_f64p))
+    return bias[: idx.shape[0]].copy()
+
+
+def attend_biased(q, K, V, b, idx, bias, scale):
+    """Attention over the kept blocks with an additive logit bias per block."""
+    q, pq = _f32(q)
+    K, pK = _f32(K)
+    V, pV = _f32(V)
+    T, d = K.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    bias, pb = _f64(bias)
+    assert bias.shape[0] == idx.shape[0]
+    o = np.empty(d, np.float64)
+    lse = ctypes.c_double()
+    lib().orc_attend_biased(pq, pK, pV, T, d, b, idx.ctypes.data_as(_i32p),
+                            idx.shape[0], pb, scale, o.ctypes.data_as(_f64p),
+                            ctypes.byref(lse))
+    return o, lse.value
+
+
+def decode_group_gated(q, K, V, b, desc_kind, tau, W=None, budget_tokens=0,
+                       sparsity_bp=0, n_local=1, n_min=0, scale=None):
+    """decode_group with the SAS log-gate bias.  Returns (idx [cnt],
+    o [G, d], lse [G], bias [cnt])."""
+    q, pq = _f32(q)
+    G, d = q.shape
+    K, pK = _f32(K)
+    V, pV = _f32(V)
+    T = K.shape[0]
+    NB = nblocks(T, b)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    if W is None:
+        Wk, pW = None, None
+    else:
+        Wk, pW = _f32(W)
+    idx = np.empty(max(NB, 1), np.int32)
+    o = np.empty((G, d), np.float64)
+    lse = np.empty(G, np.float64)
+    bias = np.empty(max(NB, 1), np.float64)
+    c = lib().orc_decode_group_gated(pq, G, pK, pV, T, d, b, desc_kind, pW,
+                                     budget_tokens, sparsity_bp, n_local, n_min,
+                                     scale, tau, idx.ctypes.data_as(_i32p), NB,
+                                     o.ctypes.data_as(_f64p), lse.ctypes.data_as(_f64p),
+                                     bias.ctypes.data_as(_f64p))
+    return idx[:c].copy(), o, lse, bias[:c].copy()

@@ -22,7 +22,9 @@
  *  [SeerR]  "SeerAttention-R: Sparse Attention Adaptation for Long Reasoning"
  *           (mlsanity.com page), section "Abstract (arXiv)".
  *  [SAS]    "Simple Attention Sparsification" (hyper.ai page), section
- *           "Method" (the o_SAS equation and the Top-K discretisation).
+ *           "Method" (the o_SAS equation, the softmax gates over the
+ *           candidate blocks, the unit gate of the current block and the
+ *           Top-K discretisation).
  *  [FD]     Flash-Decoding, cited in the [ReSA] page's reference list.
  *
  * Readings the pages leave open are marked READING and are listed, with the
@@ -340,6 +342,107 @@ ORC_API int64_t orc_decode_group(const float* q, int G, const float* K,
         orc_attend(q + (int64_t)h * d, K, V, T, d, b, idx, cnt, scale,
                    o + (int64_t)h * d, lse + h);
     if (scores) memcpy(scores, s, sizeof(double) * (size_t)NB);
+    free(s);
+    return cnt;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 8. Log-gate bias of the selected blocks (SAS)                            */
+/* ------------------------------------------------------------------------ */
+
+/* [SAS] "Method": the C candidate (historical) blocks' selector scores s
+ * become normalised gates g = softmax(s) over all C candidates; the current
+ * block keeps the unit gate g_0 = 1; the logits of a selected block's tokens
+ * get log g added inside the softmax.
+ * READING: g = softmax(tau * s) with tau > 0 (tau = 1 is the page's form;
+ * the scores here are the method's block scores, not a trained selector's
+ * logits, so their scale is left to the caller); every local block counts
+ * as the current block (bias 0).
+ * s: [NB] with the candidates 0..NC-1 scored; idx/cnt: a selection as
+ * orc_select returns it; bias: [cnt], log g of each selected block. */
+ORC_API void orc_gate_bias(const double* s, int64_t NB, int n_local, double tau,
+                           const int32_t* idx, int64_t cnt, double* bias) {
+    int64_t nl = (n_local < NB) ? n_local : NB;
+    int64_t nc = NB - nl;
+    /* log sum_c exp(tau s_c), with the largest term factored out */
+    double m = -INFINITY;
+    for (int64_t c = 0; c < nc; ++c)
+        if (tau * s[c] > m) m = tau * s[c];
+    double z = 0.0;
+    for (int64_t c = 0; c < nc; ++c) z += exp(tau * s[c] - m);
+    double log_norm = m + log(z);
+    for (int64_t k = 0; k < cnt; ++k) {
+        int64_t j = idx[k];
+        bias[k] = (j >= nc) ? 0.0 : tau * s[j] - log_norm;
+    }
+}
+
+/* [SAS] "Method", the o_SAS equation: softmax over the selected blocks'
+ * tokens of z_t + bias(block of t), z_t = scale q.k_t; two passes, exact.
+ * bias: [nidx], the additive logit bias of each selected block. */
+ORC_API void orc_attend_biased(const float* q, const float* K, const float* V,
+                               int64_t T, int d, int b, const int32_t* idx,
+                               int64_t nidx, const double* bias, double scale,
+                               double* o, double* lse) {
+    double m = -INFINITY;
+    for (int64_t k = 0; k < nidx; ++k) {
+        int64_t t0 = (int64_t)idx[k] * b;
+        int64_t t1 = t0 + b;
+        if (t1 > T) t1 = T;
+        for (int64_t t = t0; t < t1; ++t) {
+            double z = 0.0;
+            for (int i = 0; i < d; ++i) z += (double)q[i] * K[t * d + i];
+            z = z * scale + bias[k];
+            if (z > m) m = z;
+        }
+    }
+    double l = 0.0;
+    for (int i = 0; i < d; ++i) o[i] = 0.0;
+    for (int64_t k = 0; k < nidx; ++k) {
+        int64_t t0 = (int64_t)idx[k] * b;
+        int64_t t1 = t0 + b;
+        if (t1 > T) t1 = T;
+        for (int64_t t = t0; t < t1; ++t) {
+            double z = 0.0;
+            for (int i = 0; i < d; ++i) z += (double)q[i] * K[t * d + i];
+            z = z * scale + bias[k];
+            double p = exp(z - m);
+            l += p;
+            for (int i = 0; i < d; ++i) o[i] += p * V[t * d + i];
+        }
+    }
+    for (int i = 0; i < d; ++i) o[i] /= l;
+    *lse = m + log(l);
+}
+
+/* A whole decode step with the SAS log-gate bias: orc_decode_group's
+ * descriptors, scores, count and selection, then the biased attention.
+ * bias (optional, may be NULL): [idx_cap] receives log g of each selected
+ * block. */
+ORC_API int64_t orc_decode_group_gated(const float* q, int G, const float* K,
+                                       const float* V, int64_t T, int d, int b,
+                                       int desc_kind, const float* W,
+                                       int64_t budget_tokens, int sparsity_bp,
+                                       int n_local, int n_min, double scale,
+                                       double tau, int32_t* idx, int64_t idx_cap,
+                                       double* o, double* lse, double* bias) {
+    int64_t NB = orc_nblocks(T, b);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(NB > 0 ? NB : 1));
+    double* o0 = (double*)malloc(sizeof(double) * (size_t)G * d);
+    double* l0 = (double*)malloc(sizeof(double) * (size_t)G);
+    int64_t cnt = orc_decode_group(q, G, K, V, T, d, b, desc_kind, W, budget_tokens,
+                                   sparsity_bp, n_local, n_min, scale, idx, idx_cap,
+                                   o0, l0, s);
+    double* g = (double*)malloc(sizeof(double) * (size_t)(cnt > 0 ? cnt : 1));
+    orc_gate_bias(s, NB, n_local, tau, idx, cnt, g);
+    for (int h = 0; h < G; ++h)
+        orc_attend_biased(q + (int64_t)h * d, K, V, T, d, b, idx, cnt, g, scale,
+                          o + (int64_t)h * d, lse + h);
+    if (bias)
+        for (int64_t k = 0; k < cnt; ++k) bias[k] = g[k];
+    free(g);
+    free(l0);
+    free(o0);
     free(s);
     return cnt;
 }

@@ -416,3 +416,156 @@ def test_decode_group_planted_blocks_are_selected():
         K[j * b:(j + 1) * b] += (6.0 * u).astype(np.float32)
     idx, _, _ = O.decode_group(q, K, V, b, 0, budget_tokens=4 * 64, n_local=1, n_min=2)
     assert idx.tolist() == planted + [32]
+
+
+# --------------------------------------------------------------------------
+# Log-gate bias (SAS)
+# --------------------------------------------------------------------------
+
+def _bias_mask(T, b, idx, bias):
+    """Per-token additive mask: the block's bias on its tokens, -inf on
+    every token of a block that is not kept."""
+    m = np.full(T, -np.inf)
+    for j, g in zip(idx, bias):
+        m[j * b:min((j + 1) * b, T)] = g
+    return m
+
+
+def test_gate_bias_equals_scipy_log_softmax():
+    """The bias of a kept candidate is scipy's log_softmax of tau*s over ALL
+    candidates (not only the kept ones); local blocks get 0.  Catches: a
+    normaliser over the kept set only, a missing tau, a local block taken as a
+    candidate, a sign error."""
+    from scipy.special import log_softmax
+    r = rng(60)
+    NB, nl, tau = 40, 3, 0.37
+    s = 20 * r.standard_normal(NB - nl)
+    idx = np.array([1, 5, 17, 30, 37, 38, 39], np.int32)
+    g = O.gate_bias(s, NB, nl, tau, idx)
+    ref = log_softmax(tau * s)
+    np.testing.assert_allclose(g[:4], ref[[1, 5, 17, 30]], rtol=0, atol=1e-13)
+    assert g[4:].tolist() == [0.0, 0.0, 0.0]
+
+
+def test_gate_bias_uniform_scores_is_minus_log_c():
+    """Equal scores (or tau = 0): every candidate's gate is 1/C."""
+    NB, nl = 25, 2
+    idx = np.arange(NB, dtype=np.int32)
+    for s, tau in [(np.full(NB - nl, 3.5), 1.0), (np.arange(NB - nl, dtype=float), 0.0)]:
+        g = O.gate_bias(s, NB, nl, tau, idx)
+        np.testing.assert_allclose(g[:NB - nl], -math.log(NB - nl), rtol=0, atol=1e-14)
+        assert g[NB - nl:].tolist() == [0.0] * nl
+
+
+def test_gate_bias_shift_invariant_and_normalised():
+    """softmax is unchanged by a common shift of the scores, and the gates of
+    all candidates sum to one, also with scores far beyond exp's range (the
+    largest term must be factored out)."""
+    r = rng(61)
+    NB, nl, tau = 64, 1, 2.0
+    s = 400 * r.standard_normal(NB - nl)
+    idx = np.arange(NB, dtype=np.int32)
+    g1 = O.gate_bias(s, NB, nl, tau, idx)
+    g2 = O.gate_bias(s + 1234.5, NB, nl, tau, idx)
+    np.testing.assert_allclose(g1, g2, rtol=0, atol=1e-9)
+    assert np.all(np.isfinite(g1[:NB - nl]) | (g1[:NB - nl] == -np.inf))
+    assert abs(np.exp(g1[:NB - nl]).sum() - 1.0) < 1e-12
+
+
+def test_attend_biased_equals_sdpa_with_float_mask():
+    """Attention with a per-block logit bias equals torch SDPA given the bias
+    expanded to a float token mask.  Catches: the bias multiplied by the
+    softmax scale, added to the wrong block, or left out of the lse."""
+    r = rng(62)
+    T, b, d = 517, 32, 16
+    K = r.standard_normal((T, d)).astype(np.float32)
+    V = r.standard_normal((T, d)).astype(np.float32)
+    q = r.standard_normal(d).astype(np.float32)
+    NB = (T + b - 1) // b
+    idx = np.array([0, 3, 4, 9, 15, NB - 1], np.int32)
+    bias = r.uniform(-4, 0, idx.shape[0])
+    scale = 1 / math.sqrt(d)
+    o, lse = O.attend_biased(q, K, V, b, idx, bias, scale)
+    m = _bias_mask(T, b, idx, bias)
+    qt = torch.from_numpy(q.astype(np.float64))[None, None, None, :]
+    Kt = torch.from_numpy(K.astype(np.float64))[None, None]
+    Vt = torch.from_numpy(V.astype(np.float64))[None, None]
+    mt = torch.from_numpy(m)[None, None, None, :]
+    o_ref = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt, attn_mask=mt,
+                                                             scale=scale)[0, 0, 0].numpy()
+    z = scale * (K.astype(np.float64) @ q.astype(np.float64)) + m
+    np.testing.assert_allclose(o, o_ref, rtol=1e-10, atol=1e-12)
+    assert abs(lse - logsumexp(z)) < 1e-10
+
+
+def test_attend_biased_equal_keys_weighted_mean():
+    """With one shared key the weights are exp(bias) per token: o is the mean
+    of V weighted by exp(bias_k) over every token of block k, and
+    lse = scale*q.k + ln sum_k n_k exp(bias_k)."""
+    r = rng(63)
+    T, b, d = 200, 16, 8
+    k = r.standard_normal(d).astype(np.float32)
+    K = np.tile(k, (T, 1))
+    V = r.standard_normal((T, d)).astype(np.float32)
+    q = r.standard_normal(d).astype(np.float32)
+    idx = np.array([2, 7, 12], np.int32)          # block 12 is the partial one
+    bias = np.array([-1.0, 0.0, -2.5])
+    o, lse = O.attend_biased(q, K, V, b, idx, bias, 0.25)
+    num = np.zeros(d)
+    den = 0.0
+    for j, g in zip(idx, bias):
+        rows = V[j * b:min((j + 1) * b, T)].astype(np.float64)
+        num += math.exp(g) * rows.sum(0)
+        den += math.exp(g) * rows.shape[0]
+    np.testing.assert_allclose(o, num / den, rtol=1e-12, atol=1e-14)
+    z = 0.25 * float(np.dot(q.astype(np.float64), k.astype(np.float64)))
+    assert abs(lse - (z + math.log(den))) < 1e-12
+
+
+def test_attend_biased_zero_bias_is_attend():
+    r = rng(64)
+    T, b, d = 300, 64, 8
+    K = r.standard_normal((T, d)).astype(np.float32)
+    V = r.standard_normal((T, d)).astype(np.float32)
+    q = r.standard_normal(d).astype(np.float32)
+    idx = np.array([0, 2, 4], np.int32)
+    o1, l1 = O.attend_biased(q, K, V, b, idx, np.zeros(3), 0.4)
+    o2, l2 = O.attend(q, K, V, b, idx, 0.4)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-15)
+    assert abs(l1 - l2) < 1e-15
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_decode_group_gated_matches_selection_and_sdpa(kind):
+    """The gated step keeps the ungated step's selection, and its outputs are
+    torch SDPA with log_softmax(tau*s) of the candidate scores (0 on the local
+    blocks) as the float mask."""
+    from scipy.special import log_softmax
+    r = rng(65 + kind)
+    T, b, d, G, nl = 1500, 64, 16, 4, 2
+    K = r.standard_normal((T, d)).astype(np.float32)
+    V = r.standard_normal((T, d)).astype(np.float32)
+    q = r.standard_normal((G, d)).astype(np.float32)
+    W = r.standard_normal((d, d)).astype(np.float32) if kind else None
+    tau = 0.05
+    idx0, _, _, s = O.decode_group(q, K, V, b, kind, W=W, budget_tokens=6 * 64,
+                                   n_local=nl, n_min=2, want_scores=True)
+    idx, o, lse, bias = O.decode_group_gated(q, K, V, b, kind, tau, W=W,
+                                             budget_tokens=6 * 64, n_local=nl, n_min=2)
+    assert idx.tolist() == idx0.tolist()
+    NB = (T + b - 1) // b
+    ls = log_softmax(tau * s[:NB - nl])
+    ref_bias = np.array([ls[j] if j < NB - nl else 0.0 for j in idx])
+    np.testing.assert_allclose(bias, ref_bias, rtol=0, atol=1e-12)
+    m = _bias_mask(T, b, idx, ref_bias)
+    scale = 1 / math.sqrt(d)
+    for h in range(G):
+        qt = torch.from_numpy(q[h].astype(np.float64))[None, None, None, :]
+        Kt = torch.from_numpy(K.astype(np.float64))[None, None]
+        Vt = torch.from_numpy(V.astype(np.float64))[None, None]
+        mt = torch.from_numpy(m)[None, None, None, :]
+        o_ref = torch.nn.functional.scaled_dot_product_attention(
+            qt, Kt, Vt, attn_mask=mt, scale=scale)[0, 0, 0].numpy()
+        z = scale * (K.astype(np.float64) @ q[h].astype(np.float64)) + m
+        np.testing.assert_allclose(o[h], o_ref, rtol=1e-10, atol=1e-12)
+        assert abs(lse[h] - logsumexp(z)) < 1e-10
