@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--cpu-steps", type=int, default=40)
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads (sparsity sweep, 32K, batched, ReSA loop)")
+    ap.add_argument("--gate-tau", type=float, default=None,
+                    help="also time the headline workload with the log-gate bias "
+                         "(select writes it, bsa_sparse_decode_gated adds it) at this tau")
     ap.add_argument("--resa-sweep", action="store_true",
                     help="also run the ragged ReSA loop over f in {16,32,64,128} x p in "
                          "{0.9,0.95,0.98} and compare its bytes with 1/b + (1-p) + 1/f")
@@ -175,6 +178,9 @@ class Run:
         self.cnt = [torch.empty(w.B, w.Hkv, dtype=torch.int32, device=dev) for _ in range(layers)]
         self.o = [torch.empty(w.B, w.Hq, w.d, dtype=self.tdt, device=dev) for _ in range(layers)]
         self.lse = [torch.empty(w.B, w.Hq, dtype=torch.float32, device=dev) for _ in range(layers)]
+        self.gate_tau = None  # set to a float to run the gated step
+        self.gbias = [torch.zeros(w.B, w.Hkv, n_max_all, dtype=torch.float32, device=dev)
+                      for _ in range(layers)]
         if self.f:
             self.o_r = [torch.empty(w.B, w.Hq, self.f, w.d, dtype=self.tdt, device=dev)
                         for _ in range(layers)]
@@ -210,12 +216,20 @@ class Run:
             c = self.caches[l]
             # append + select (the append shares the scoring launch); idx rows
             # are n_max long (the buffer fits the largest n_max of the sweep)
+            gated = self.gate_tau is not None
+            P.gate_tau = self.gate_tau if gated else 0.0
+            P.gate_bias = self.gbias[l] if gated else None
             bsa.append_select(self.L, c, inp["kn"][i, l], inp["vn"][i, l], inp["q"][i, l], P,
                               self.idx[l], self.cnt[l], self.ws[l])
             if ev is not None:
                 ev[l][0].record()
-            bsa.sparse_decode(self.L, c, inp["q"][i, l], self.idx[l], self.cnt[l], P.n_max,
-                              self.scale, self.o[l], self.lse[l], self.ws[l])
+            if gated:
+                bsa.sparse_decode_gated(self.L, c, inp["q"][i, l], self.idx[l], self.cnt[l],
+                                        self.gbias[l], P.n_max, self.scale, self.o[l], self.lse[l],
+                                        self.ws[l])
+            else:
+                bsa.sparse_decode(self.L, c, inp["q"][i, l], self.idx[l], self.cnt[l], P.n_max,
+                                  self.scale, self.o[l], self.lse[l], self.ws[l])
             if ev is not None:
                 ev[l][1].record()
             if rect:
@@ -472,6 +486,16 @@ def main():
         "eager_us_per_step_layer": head["eager_us_per_step_layer"],
         "workloads": [head] + [summarize(w, bp, args.layers, m)[1] for bp, m in results[1:]],
     }
+    if args.gate_tau is not None:
+        run.gate_tau = args.gate_tau
+        mg = measure(run, args.steps, args.warmup, seed=2)
+        run.gate_tau = None
+        gh = summarize(w, bp0, args.layers, mg)[1]
+        gh["gate_tau"] = args.gate_tau
+        gh["decode_us_avg"] = round(mg["decode_us_avg"], 3)
+        gh["note"] = "same step with the log-gate bias written by select and added by the decode"
+        out["gated"] = gh
+        print(f"# gated tau={args.gate_tau}: {json.dumps(mg)}", file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(run, args.cpu_steps)
     del run

@@ -22,8 +22,8 @@ DESC_MINMAX, DESC_MEANPOOL = 0, 1
 OP_SELECT, OP_DECODE, OP_RECTIFY = 1, 2, 3
 
 EXPORTS = ("bsa_build_block_desc", "bsa_select_blocks", "bsa_append_select",
-           "bsa_sparse_decode", "bsa_rectify_chunk", "bsa_workspace_size", "bsa_block_count",
-           "bsa_status_string")
+           "bsa_sparse_decode", "bsa_sparse_decode_gated", "bsa_rectify_chunk",
+           "bsa_workspace_size", "bsa_block_count", "bsa_status_string")
 
 
 class BsaError(RuntimeError):
@@ -46,7 +46,8 @@ class c_cache(ctypes.Structure):
 class c_select_params(ctypes.Structure):
     _fields_ = [("budget_tokens", ctypes.c_int32), ("sparsity_bp", ctypes.c_int32),
                 ("n_local", ctypes.c_int32), ("n_min", ctypes.c_int32),
-                ("n_max", ctypes.c_int32), ("gate_w", ctypes.c_void_p)]
+                ("n_max", ctypes.c_int32), ("gate_w", ctypes.c_void_p),
+                ("gate_tau", ctypes.c_float), ("gate_bias", ctypes.c_void_p)]
 
 
 _lib = None
@@ -67,6 +68,8 @@ def lib():
     L.bsa_select_blocks.argtypes = [pl, pc, vp, pp, vp, vp, vp, sz, vp]
     L.bsa_append_select.argtypes = [pl, pc, vp, vp, vp, pp, vp, vp, vp, sz, vp]
     L.bsa_sparse_decode.argtypes = [pl, pc, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
+    L.bsa_sparse_decode_gated.argtypes = [pl, pc, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp,
+                                          vp, sz, vp]
     L.bsa_rectify_chunk.argtypes = [pl, pc, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     L.bsa_workspace_size.argtypes = [pl, i32, i32]
     L.bsa_workspace_size.restype = sz
@@ -74,8 +77,8 @@ def lib():
     L.bsa_block_count.restype = i32
     L.bsa_status_string.argtypes = [ctypes.c_int]
     L.bsa_status_string.restype = ctypes.c_char_p
-    for fn in (L.bsa_build_block_desc, L.bsa_select_blocks, L.bsa_sparse_decode,
-               L.bsa_rectify_chunk):
+    for fn in (L.bsa_build_block_desc, L.bsa_select_blocks, L.bsa_append_select,
+               L.bsa_sparse_decode, L.bsa_sparse_decode_gated, L.bsa_rectify_chunk):
         fn.restype = ctypes.c_int
     _lib = L
     return L
@@ -136,10 +139,14 @@ class SelectParams:
     n_min: int = 0
     n_max: int = 0
     gate_w: Optional[object] = None  # torch bf16 [d, d] on the device
+    gate_tau: float = 0.0
+    gate_bias: Optional[object] = None  # torch fp32 [B, Hkv, n_max] on the device, OUT
 
     def c(self):
         return c_select_params(self.budget_tokens, self.sparsity_bp, self.n_local, self.n_min,
-                               self.n_max, None if self.gate_w is None else self.gate_w.data_ptr())
+                               self.n_max, None if self.gate_w is None else self.gate_w.data_ptr(),
+                               float(self.gate_tau),
+                               None if self.gate_bias is None else self.gate_bias.data_ptr())
 
 
 @dataclass
@@ -231,6 +238,17 @@ def sparse_decode(layout: Layout, cache: Cache, q, idx, cnt, n_max: int, softmax
                                  _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream))
     _check(st, "bsa_sparse_decode")
+
+
+def sparse_decode_gated(layout: Layout, cache: Cache, q, idx, cnt, gate_bias, n_max: int,
+                        softmax_scale: float, o, lse, ws, stream=None):
+    """sparse_decode with gate_bias [B, Hkv, n_max] (fp32) added to the
+    logits of every token of block idx[..., k]."""
+    st = lib().bsa_sparse_decode_gated(ctypes.byref(layout.c()), ctypes.byref(cache.c()),
+                                       _ptr(q), _ptr(idx), _ptr(cnt), _ptr(gate_bias), int(n_max),
+                                       float(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws),
+                                       ws.numel() * ws.element_size(), _stream(stream))
+    _check(st, "bsa_sparse_decode_gated")
 
 
 def rectify_chunk(layout: Layout, cache: Cache, q, k_new, v_new, f: int, softmax_scale: float,

@@ -101,10 +101,39 @@ bsa_status check_select_params(const bsa_layout* L, const bsa_select_params* P) 
     const int need = block_count(L->max_blocks, L->block, P->budget_tokens, P->sparsity_bp,
                                  P->n_local, P->n_min);
     if (P->n_max < need) return BSA_ERR_PARAM;
+    if (P->gate_bias && !(isfinite(P->gate_tau) && P->gate_tau >= 0.f)) return BSA_ERR_PARAM;
     return BSA_OK;
 }
 
 bsa_status hip_status(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
+
+bsa_status sparse_decode(const bsa_layout* layout, const bsa_cache* cache, const void* q,
+                         const int32_t* idx, const int32_t* cnt, const float* bias, int32_t n_max,
+                         float softmax_scale, void* o, float* lse, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    bsa_status st = check_layout(layout);
+    if (st != BSA_OK) return st;
+    if ((st = check_cache(cache)) != BSA_OK) return st;
+    if (!q || !idx || !cnt || !o || !lse || !ws) return BSA_ERR_NULL;
+    if (n_max < 1 || n_max > layout->max_blocks) return BSA_ERR_PARAM;
+    if (!scale_ok(softmax_scale)) return BSA_ERR_PARAM;
+    const CacheArgs c = make_args(layout, cache);
+    const DecodeWs w = decode_ws(c, n_max);
+    if (ws_bytes < w.total) return BSA_ERR_WORKSPACE;
+    DecodeArgs a;
+    a.q = q;
+    a.idx = idx;
+    a.cnt = cnt;
+    a.n_max = n_max;
+    a.splits = w.splits;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.bias = bias;
+    a.o_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.o_part);
+    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.lse_part);
+    a.o = o;
+    a.lse = lse;
+    return hip_status(launch_decode(c, a, stream));
+}
 
 }  // namespace
 
@@ -184,6 +213,8 @@ bsa_status bsa_select_blocks(const bsa_layout* layout, const bsa_cache* cache, c
     s.idx = idx;
     s.cnt = cnt;
     s.scores = static_cast<float*>(ws);
+    s.gate_tau = params->gate_tau;
+    s.gate_bias = params->gate_bias;
     return hip_status(launch_select(c, s, stream));
 }
 
@@ -210,6 +241,8 @@ bsa_status bsa_append_select(const bsa_layout* layout, const bsa_cache* cache, c
     s.idx = idx;
     s.cnt = cnt;
     s.scores = static_cast<float*>(ws);
+    s.gate_tau = params->gate_tau;
+    s.gate_bias = params->gate_bias;
     return hip_status(launch_append_select(c, k_new, v_new, s, stream));
 }
 
@@ -217,27 +250,18 @@ bsa_status bsa_sparse_decode(const bsa_layout* layout, const bsa_cache* cache, c
                              const int32_t* idx, const int32_t* cnt, int32_t n_max,
                              float softmax_scale, void* o, float* lse, void* ws,
                              size_t ws_bytes, hipStream_t stream) {
-    bsa_status st = check_layout(layout);
-    if (st != BSA_OK) return st;
-    if ((st = check_cache(cache)) != BSA_OK) return st;
-    if (!q || !idx || !cnt || !o || !lse || !ws) return BSA_ERR_NULL;
-    if (n_max < 1 || n_max > layout->max_blocks) return BSA_ERR_PARAM;
-    if (!scale_ok(softmax_scale)) return BSA_ERR_PARAM;
-    const CacheArgs c = make_args(layout, cache);
-    const DecodeWs w = decode_ws(c, n_max);
-    if (ws_bytes < w.total) return BSA_ERR_WORKSPACE;
-    DecodeArgs a;
-    a.q = q;
-    a.idx = idx;
-    a.cnt = cnt;
-    a.n_max = n_max;
-    a.splits = w.splits;
-    a.scale_log2 = softmax_scale * kLog2e;
-    a.o_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.o_part);
-    a.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.lse_part);
-    a.o = o;
-    a.lse = lse;
-    return hip_status(launch_decode(c, a, stream));
+    return sparse_decode(layout, cache, q, idx, cnt, nullptr, n_max, softmax_scale, o, lse, ws,
+                         ws_bytes, stream);
+}
+
+bsa_status bsa_sparse_decode_gated(const bsa_layout* layout, const bsa_cache* cache,
+                                   const void* q, const int32_t* idx, const int32_t* cnt,
+                                   const float* gate_bias, int32_t n_max, float softmax_scale,
+                                   void* o, float* lse, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+    if (!gate_bias) return BSA_ERR_NULL;
+    return sparse_decode(layout, cache, q, idx, cnt, gate_bias, n_max, softmax_scale, o, lse, ws,
+                         ws_bytes, stream);
 }
 
 bsa_status bsa_rectify_chunk(const bsa_layout* layout, const bsa_cache* cache, const void* q,

@@ -186,6 +186,11 @@ __device__ __forceinline__ uint32_t float_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The float a key came from (-0 comes back as +0).
+__device__ __forceinline__ float key_float(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
 // Kept-block count for NB blocks ("Rectified Sparse Attention ...", Key
 // points: dynamic top-n with local blocks and a minimum count; the token
 // budget of "SeerAttention-R", Abstract).  p is the skipped fraction in basis

@@ -33,6 +33,8 @@ struct SelectArgs {
     int32_t* idx;
     int32_t* cnt;
     float* scores;  // workspace [B*Hkv][score_stride(max_blocks)]
+    float gate_tau;
+    float* gate_bias;  // nullptr, or [B*Hkv][n_max]: log-gate bias per idx entry
 };
 hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t stream);
 // Append of one token per sequence (kModeAppend, n_new = 1) and selection,
@@ -51,6 +53,7 @@ struct DecodeArgs {
     int n_max;
     int splits;  // S: partials per (sequence, query head)
     float scale_log2;  // softmax_scale * log2(e)
+    const float* bias;  // nullptr, or [B*Hkv][n_max]: natural-log logit bias per idx entry
     float* o_part;     // [B*Hq][S][d]
     float* lse_part;   // [B*Hq][S]  (base-2 log-sum-exp of the scaled logits)
     void* o;

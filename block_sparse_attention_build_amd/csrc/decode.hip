@@ -25,6 +25,9 @@
 // once per head.  Each unit leaves a partial (max, sum, O) in LDS; the units
 // are merged in unit order and the workgroup writes one normalised partial
 // (o, base-2 lse) per head, which the merge kernel combines across splits.
+// The gated instance ("Simple Attention Sparsification", Method: the o_SAS
+// equation) adds each kept block's log-gate bias to its tokens' logits; the
+// bias rides along with the block's page id, one wave-uniform value per tile.
 //
 // fp32 path.  Same split structure, plain VALU arithmetic (no fp32 matrix
 // operand layout is defined for the pages); used by the small fp32 cases.
@@ -49,6 +52,8 @@ namespace {
 #ifndef BSA_DECODE_UNIT_LDS
 #define BSA_DECODE_UNIT_LDS (112 * 1024)  // LDS bytes for the per-unit partials
 #endif
+constexpr int kLdsBytes = 160 * 1024;      // LDS of one CU
+constexpr int kMaxSplitBlocks = 4096;      // kept blocks one split may cover
 constexpr int kThreads = 256;     // fp32 kernel
 constexpr int kWaves = kThreads / kWave;
 constexpr int kDecThreads = 512;  // bf16 kernel: 8 waves
@@ -104,7 +109,7 @@ __device__ __forceinline__ void merge_waves_and_store(const float* sm, const flo
 // (running max, sum, unnormalised O) in LDS, and the units are merged in
 // unit order at the end, so the result does not depend on which wave took
 // which unit.
-template <int D, int BLK>
+template <int D, int BLK, bool GATE>
 __global__ __launch_bounds__(kDecThreads)
 __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf16_kernel(
     DecodeParams p) {
@@ -119,6 +124,7 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     float* uo = ul + MU * 16;            // [MU][G][D] unnormalised O
     int* s_blk = reinterpret_cast<int*>(uo + MU * G * D);  // [max_blocks_per_wg]
     int* s_page = s_blk + p.max_blocks_per_wg;              // [max_blocks_per_wg]
+    float* s_bias = reinterpret_cast<float*>(s_page + p.max_blocks_per_wg);  // GATE only
     __shared__ int s_next;
 
     const CacheArgs& c = p.c;
@@ -164,6 +170,7 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
         const bool kept = pb0 + i < cnt;
         s_blk[i] = kept ? blk : 0;
         s_page[i] = kept ? ptrow[blk] : 0;
+        if (GATE) s_bias[i] = kept ? a.bias[static_cast<int64_t>(grp) * a.n_max + pb0 + i] * kLog2e : 0.f;
     }
     if (threadIdx.x == 0) s_next = 0;
     __syncthreads();
@@ -190,12 +197,15 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
         if (lane == 0) v = atomicAdd(&s_next, 1);
         return __builtin_amdgcn_readfirstlane(v);
     };
-    // tile u -> (element offset of its 32-token run, tokens valid in it)
-    auto resolve = [&](int u, int64_t& off, int& nvalid) __attribute__((always_inline)) {
+    // tile u -> (element offset of its 32-token run, tokens valid in it,
+    // base-2 logit bias of its block)
+    auto resolve = [&](int u, int64_t& off, int& nvalid, float& b2) __attribute__((always_inline)) {
         const int pi = u / TPB;
         const int r = u - pi * TPB;
         const int blk = __builtin_amdgcn_readfirstlane(s_blk[pi - pb0]);
         const int page = __builtin_amdgcn_readfirstlane(s_page[pi - pb0]);
+        b2 = GATE ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_bias[pi - pb0])))
+                  : 0.f;
         nvalid = T - (blk * BLK + 32 * r);
         off = (static_cast<int64_t>(page) * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) + 32 * r * D;
     };
@@ -208,7 +218,7 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
         for (int n = 0; n < NT; ++n) vr[n] = ldg16(vl + off + n * 512);
     };
     // one tile: QK, online softmax, PV; NEXT: also issue the next tile's loads
-    auto step = [&](const int nvalid, const bool next, const int64_t off_nxt)
+    auto step = [&](const int nvalid, const float b2, const bool next, const int64_t off_nxt)
                     __attribute__((always_inline)) {
         floatx4 sacc[2];
 #pragma unroll
@@ -224,7 +234,8 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int tok = (k < 4) ? (4 * g + k) : (16 + 4 * g + k - 4);
-            x[k] = (tok < nvalid) ? sacc[k >> 2][k & 3] * sl2 : -INFINITY;
+            const float z = GATE ? fmaf(sacc[k >> 2][k & 3], sl2, b2) : sacc[k >> 2][k & 3] * sl2;
+            x[k] = (tok < nvalid) ? z : -INFINITY;
         }
         float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                            fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -309,7 +320,8 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
         int t_end = min(t + UT, uend);
         int64_t off = 0;
         int nv = 0;
-        resolve(t, off, nv);
+        float b2 = 0.f;
+        resolve(t, off, nv, b2);
         load_k(off);
         load_v(off);
         while (true) {
@@ -322,15 +334,17 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
             if (nunit >= n_units) break;
             int64_t off_nxt = 0;
             int nv_nxt = 0;
-            resolve(nt, off_nxt, nv_nxt);
-            step(nv, true, off_nxt);
+            float b2_nxt = 0.f;
+            resolve(nt, off_nxt, nv_nxt, b2_nxt);
+            step(nv, b2, true, off_nxt);
             if (nunit != unit) flush(unit);
             unit = nunit;
             t = nt;
             t_end = nend;
             nv = nv_nxt;
+            b2 = b2_nxt;
         }
-        step(nv, false, 0);
+        step(nv, b2, false, 0);
         flush(unit);
     }
     __syncthreads();
@@ -413,6 +427,7 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeParams p) {
         const int nvalid = min(32, T - tok0);
         if (nvalid <= 0) continue;
         const int64_t page = ptrow[blk];
+        const float b2 = a.bias ? a.bias[static_cast<int64_t>(grp) * a.n_max + pi] * kLog2e : 0.f;
         const float* kt = kpool + (page * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) + 32 * r * D;
         const float* vt = vpool + (page * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) + 32 * r * D;
 #pragma unroll
@@ -422,7 +437,7 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeParams p) {
             if (lane < nvalid) {
                 float acc = 0.f;
                 for (int i = 0; i < D; ++i) acc += qs[h * D + i] * kt[lane * D + i];
-                z = acc * a.scale_log2;
+                z = fmaf(acc, a.scale_log2, b2);
             }
             const float mt = wave_max(z);
             const float m_new = fmaxf(m[h], mt);
@@ -552,19 +567,26 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 
 template <int D, int BLK>
 hipError_t launch_bf16(DecodeParams p, hipStream_t stream) {
+    const bool gate = p.a.bias != nullptr;
     // units: as many LDS partial slots as the budget holds, each unit at
     // least two tiles; the split's tiles / units tiles per unit
     const int tiles = (p.a.n_max * (BLK / 32) + p.a.splits - 1) / p.a.splits;
     const int unit_bytes = static_cast<int>(sizeof(float)) * (32 + p.c.G * D);
-    const int slots = BSA_DECODE_UNIT_LDS / unit_bytes;
+    // the split's block ids, page ids (and biases) take what they need; the
+    // unit partials get the configured budget or what remains of the CU's LDS
+    const int id_bytes = (gate ? 3 : 2) * static_cast<int>(sizeof(int)) * p.max_blocks_per_wg;
+    const int budget = min(BSA_DECODE_UNIT_LDS, kLdsBytes - 256 - id_bytes);
+    const int slots = budget / unit_bytes;
     int ut = (tiles + slots - 1) / slots;
     if (ut < 2) ut = 2;
     p.unit_tiles = ut;
     p.max_units = (tiles + ut - 1) / ut;
-    const size_t shm = static_cast<size_t>(unit_bytes) * p.max_units +
-                       2 * sizeof(int) * p.max_blocks_per_wg;
+    const size_t shm = static_cast<size_t>(unit_bytes) * p.max_units + id_bytes;
     dim3 grid(p.a.splits, p.c.B * p.c.Hkv);
-    hipLaunchKernelGGL((decode_bf16_kernel<D, BLK>), grid, dim3(kDecThreads), shm, stream, p);
+    if (gate)
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, true>), grid, dim3(kDecThreads), shm, stream, p);
+    else
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false>), grid, dim3(kDecThreads), shm, stream, p);
     return hipGetLastError();
 }
 
@@ -591,12 +613,15 @@ hipError_t launch_f32(const DecodeParams& p, hipStream_t stream) {
 
 int decode_splits(const CacheArgs& c, int n_max) {
     // about BSA_DECODE_TARGET_WGS workgroups over the chip (one per CU for
-    // the bf16 kernel), at least 4 tiles in every split.
+    // the bf16 kernel), at least 4 tiles in every split, and at most
+    // kMaxSplitBlocks blocks in a split (their ids are staged in LDS).
     const int groups = c.B * c.Hkv;
     const int tiles = n_max * (c.block / 32);
     int S = (BSA_DECODE_TARGET_WGS + groups - 1) / groups;
     const int cap = (tiles + 3) / 4;
     if (S > cap) S = cap;
+    const int least = (n_max + kMaxSplitBlocks - 1) / kMaxSplitBlocks;
+    if (S < least) S = least;
     if (S < 1) S = 1;
     return S;
 }

@@ -266,6 +266,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     __shared__ int n_alive_s;
     __shared__ uint32_t res_s[2];
     __shared__ uint32_t red_min[kTopnWaves], red_max[kTopnWaves];
+    __shared__ float red_z[kTopnWaves];
 
     const int grp = blockIdx.x;
     const int s = grp / c.Hkv;
@@ -298,10 +299,50 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         for (int r = 0; r < KPT; ++r) key[r] = float_key(sc[(base + r < NC) ? base + r : 0]);
     }
 
+    // Log-gate bias ("Simple Attention Sparsification", Method): gates are
+    // softmax(tau * s) over all NC candidates, so a kept candidate's bias is
+    // tau * (s_j - smax) - ln sum_c exp(tau * (s_c - smax)).  The red_max
+    // slots are read before the second barrier and rewritten only after it.
+    float* bias_out = a.gate_bias ? a.gate_bias + static_cast<int64_t>(grp) * a.n_max : nullptr;
+    float g_smax = 0.f, g_lnz = 0.f;
+    if (bias_out && NC > 0) {
+        uint32_t lmax = 0u;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r)
+            if (base + r < NC) lmax = max(lmax, key[r]);
+        lmax = wave_max_u32(lmax);
+        if (lane == 0) red_max[wave] = lmax;
+        __syncthreads();
+        uint32_t kmx = 0u;
+#pragma unroll
+        for (int w = 0; w < kTopnWaves; ++w) kmx = max(kmx, red_max[w]);
+        g_smax = key_float(kmx);
+        float z = 0.f;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r)
+            if (base + r < NC) z += expf(a.gate_tau * (key_float(key[r]) - g_smax));
+        z = wave_sum(z);
+        if (lane == 0) red_z[wave] = z;
+        __syncthreads();
+        float zt = 0.f;
+#pragma unroll
+        for (int w = 0; w < kTopnWaves; ++w) zt += red_z[w];
+        g_lnz = logf(zt);
+    }
+    auto gate = [&](uint32_t k) __attribute__((always_inline)) {
+        return a.gate_tau * (key_float(k) - g_smax) - g_lnz;
+    };
+
     // mode: 0 = pick none, 1 = pick every candidate, 2 = threshold select
     const int mode = (K <= 0) ? 0 : (K >= NC ? 1 : 2);
     if (mode == 1) {
-        for (int j = tid; j < NC; j += kTopnThreads) out[j] = j;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            if (base + r < NC) {
+                out[base + r] = base + r;
+                if (bias_out) bias_out[base + r] = gate(key[r]);
+            }
+        }
     }
     uint32_t tau = 0;
     int need_eq = 0;
@@ -467,7 +508,10 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
                 take = eq_rank < need_eq;
                 ++eq_rank;
             }
-            if (take && pos < a.n_max) out[pos] = base + r;
+            if (take && pos < a.n_max) {
+                out[pos] = base + r;
+                if (bias_out) bias_out[pos] = gate(key[r]);
+            }
             pos += take ? 1 : 0;
         }
     }
@@ -475,6 +519,8 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     // local blocks follow the picked candidates (their ids are the largest)
     for (int t = tid; t < nl; t += kTopnThreads) out[picked + t] = NC + t;
     for (int t = picked + nl + tid; t < a.n_max; t += kTopnThreads) out[t] = -1;
+    if (bias_out)
+        for (int t = picked + tid; t < a.n_max; t += kTopnThreads) bias_out[t] = 0.f;
     if (tid == 0) a.cnt[grp] = picked + nl;
 }
 

@@ -137,7 +137,16 @@ typedef struct bsa_cache {
  *         = ceil((10000 - sparsity_bp) * NB / 10000)  otherwise
  *   n     = min(NB, max(n_req, n_min, min(n_local, NB)))
  * The last min(n_local, NB) blocks are always kept; the rest of the n are
- * the best-scoring other blocks, ties to the lower block index. */
+ * the best-scoring other blocks, ties to the lower block index.
+ *
+ * Log-gate bias ("Simple Attention Sparsification", Method: gates are a
+ * softmax over all candidate blocks' scores, the current block's gate is 1,
+ * and log g is added to a kept block's logits).  When gate_bias is set, the
+ * selecting call also writes, at the position of each kept block j in idx,
+ *   bias = log softmax(gate_tau * s)_j   over ALL C = NB - n_local candidates,
+ * 0 for a local block and 0 for the -1 padding; computed in fp32 from the
+ * fp32 scores as gate_tau * (s_j - max s) - ln sum_c exp(gate_tau * (s_c -
+ * max s)).  bsa_sparse_decode_gated consumes it. */
 typedef struct bsa_select_params {
     int32_t budget_tokens;  /* >= 0; 0 selects the sparsity rule */
     int32_t sparsity_bp;    /* p (fraction skipped) in basis points, [0, 10000) */
@@ -146,6 +155,9 @@ typedef struct bsa_select_params {
     int32_t n_max;          /* row length of idx; must be >= n for NB = max_blocks */
     const void* gate_w;     /* MEANPOOL only: W [d][d] bf16, row r = output
                                channel r; NULL for MINMAX */
+    float gate_tau;         /* >= 0, finite; read only when gate_bias is set */
+    float* gate_bias;       /* NULL, or device fp32 [B][Hkv][n_max], OUT: the
+                               log-gate bias of each entry of idx (below) */
 } bsa_select_params;
 
 /* ---------------------------------------------------------------------------
@@ -193,9 +205,11 @@ BSA_API bsa_status bsa_build_block_desc(const bsa_layout* layout, const bsa_cach
  * cnt: [B][Hkv] int32, OUT: n.
  * ws: workspace of at least bsa_workspace_size(layout, BSA_OP_SELECT, n_max)
  *   bytes (holds the scores; contents need no initialisation).
+ * gate_bias (optional): see bsa_select_params.
  * Errors: BSA_ERR_NULL, BSA_ERR_SHAPE, BSA_ERR_UNSUPPORTED, BSA_ERR_PARAM
  *   (n_local < 1, n_min < 0, budget_tokens < 0, sparsity_bp outside
- *   [0, 10000), n_max too small, gate_w missing for MEANPOOL),
+ *   [0, 10000), n_max too small, gate_w missing for MEANPOOL, gate_tau
+ *   negative or not finite while gate_bias is set),
  *   BSA_ERR_WORKSPACE, BSA_ERR_HIP.
  * ------------------------------------------------------------------------- */
 BSA_API bsa_status bsa_select_blocks(const bsa_layout* layout, const bsa_cache* cache,
@@ -239,6 +253,26 @@ BSA_API bsa_status bsa_append_select(const bsa_layout* layout, const bsa_cache* 
 BSA_API bsa_status bsa_sparse_decode(const bsa_layout* layout, const bsa_cache* cache,
                              const void* q, const int32_t* idx,
                              const int32_t* cnt, int32_t n_max,
+                             float softmax_scale, void* o, float* lse,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * bsa_sparse_decode_gated -- bsa_sparse_decode with an additive logit bias
+ * per kept block ("Simple Attention Sparsification", Method: the o_SAS
+ * equation, softmax(q K_S^T + log g_S) V_S over the kept blocks S):
+ *   z_t = softmax_scale * q_h . k_t + gate_bias[k]   for t in block idx[k],
+ * o_h and lse_h as in bsa_sparse_decode over these z_t.
+ * gate_bias: device fp32 [B][Hkv][n_max], the row layout of idx; entry k
+ *   biases every token of block idx[k] (as written by a selecting call with
+ *   bsa_select_params.gate_bias set; any finite values work).  Entries at
+ *   positions >= cnt are not read.
+ * Other arguments, workspace and errors as in bsa_sparse_decode
+ *   (BSA_ERR_NULL also for a NULL gate_bias).
+ * ------------------------------------------------------------------------- */
+BSA_API bsa_status bsa_sparse_decode_gated(const bsa_layout* layout,
+                             const bsa_cache* cache, const void* q,
+                             const int32_t* idx, const int32_t* cnt,
+                             const float* gate_bias, int32_t n_max,
                              float softmax_scale, void* o, float* lse,
                              void* ws, size_t ws_bytes, hipStream_t stream);
 

@@ -21,7 +21,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["bsa_build_block_desc", "bsa_select_blocks", "bsa_append_select",
-              "bsa_sparse_decode", "bsa_rectify_chunk", "bsa_workspace_size",
+              "bsa_sparse_decode", "bsa_sparse_decode_gated", "bsa_rectify_chunk",
+              "bsa_workspace_size",
               "bsa_status_string", "bsa_block_count"]:
         assert n in names
     assert sorted(bsa.EXPORTS) == names
@@ -130,6 +131,35 @@ def test_append_select_validation():
     assert call(P=bsa.SelectParams(sparsity_bp=9000, n_local=0, n_max=10)) == bsa.ERR_PARAM
     assert call(ws_bytes=16) == bsa.ERR_WORKSPACE
     assert call(L=L_ok(d=96)) == bsa.ERR_UNSUPPORTED
+
+
+class _FakeDev:
+    """Stands in for a device tensor in validation calls that never launch."""
+    def data_ptr(self):
+        return 0x1000
+
+
+@pytest.mark.parametrize("tau", [-0.5, float("nan"), float("inf")])
+def test_gate_tau_rejected_when_bias_requested(tau):
+    P = bsa.SelectParams(sparsity_bp=9000, n_local=2, n_max=10, gate_tau=tau,
+                         gate_bias=_FakeDev())
+    assert _select(L_ok(), P) == bsa.ERR_PARAM
+    assert bsa.block_count(P, 100, 64) == 10   # the count ignores the gate
+
+
+def test_decode_gated_validation():
+    L = L_ok()
+    C = bsa.c_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    p = ctypes.c_void_p(0x1000)
+    lib = bsa.lib()
+
+    def call(bias=p, scale=0.1, ws_bytes=1 << 30, idx=p):
+        return lib.bsa_sparse_decode_gated(ctypes.byref(L.c()), ctypes.byref(C), p, idx, p, bias,
+                                           10, scale, p, p, p, ws_bytes, None)
+    assert call(bias=None) == bsa.ERR_NULL
+    assert call(idx=None) == bsa.ERR_NULL
+    assert call(scale=-1.0) == bsa.ERR_PARAM
+    assert call(ws_bytes=64) == bsa.ERR_WORKSPACE
 
 
 def test_decode_and_rectify_validation():

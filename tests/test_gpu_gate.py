@@ -1,0 +1,206 @@
+"""GPU parity of the log-gate bias ("Simple Attention Sparsification",
+Method: softmax gates over the candidate blocks, log g added to a kept
+block's logits) against the fp64 oracle: the bias the selecting call writes
+next to each kept block id, and the gated decode that consumes it.
+
+Selection bit-exact (inputs carry a score gap at the top-n boundary).
+Bias: the kernel works from fp32 scores; a score error ds moves a bias by at
+most tau * 2 ds plus the fp32 rounding of the normaliser's sum (relative
+n_candidates * 2^-24), so the bar is tau * 2e-5 * max|s| + 1e-4 + C * 1.2e-7
+absolute.  o within 2e-2 absolute, lse within 1e-4 relative, as ungated."""
+import math
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_build_amd as bsa
+import oracle as O
+from harness import compare_step, enforce_gap, prefill, random_page_table, to_dev
+from test_gpu_parity import BF16, F32, MEAN, MINMAX, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+GATE_CASES = [
+    # dtype, d, blk, kind, Hq, Hkv, lengths, budget, bp, n_local, n_min
+    (BF16, 128, 64, MINMAX, 8, 2, [1000, 1537], 256, 0, 1, 0),
+    (BF16, 128, 128, MEAN, 8, 2, [3000, 2049], 0, 9000, 2, 0),
+    (BF16, 128, 256, MINMAX, 8, 4, [5000, 1], 0, 9500, 1, 4),   # a group with no candidate
+    (BF16, 64, 32, MINMAX, 4, 4, [777, 1025, 64, 65], 0, 8000, 1, 3),
+    (F32, 64, 64, MINMAX, 4, 1, [2049], 512, 0, 1, 2),
+    (F32, 128, 128, MEAN, 8, 2, [1500, 700], 0, 9000, 2, 0),
+]
+
+
+def _oracle_gated(L, P, q, Ks, Vs, lengths, tau, Wg):
+    G = L.Hq // L.Hkv
+    kind = 0 if L.desc_kind == MINMAX else 1
+    scale = 1.0 / math.sqrt(L.d)
+    ref, bias, smax = {}, {}, 0.0
+    for s, T in enumerate(lengths):
+        for h in range(L.Hkv):
+            qg, K, V = q[s, h * G:(h + 1) * G], Ks[s][h, :T], Vs[s][h, :T]
+            idx, o, lse, b = O.decode_group_gated(qg, K, V, L.block, kind, tau, W=Wg,
+                                                  budget_tokens=P.budget_tokens,
+                                                  sparsity_bp=P.sparsity_bp,
+                                                  n_local=P.n_local, n_min=P.n_min, scale=scale)
+            _, _, _, sc = O.decode_group(qg, K, V, L.block, kind, W=Wg,
+                                         budget_tokens=P.budget_tokens,
+                                         sparsity_bp=P.sparsity_bp, n_local=P.n_local,
+                                         n_min=P.n_min, scale=scale, want_scores=True)
+            fin = sc[np.isfinite(sc)]
+            if fin.size:
+                smax = max(smax, float(np.abs(fin).max()))
+            ref[(s, h)] = (idx, o, lse)
+            bias[(s, h)] = b
+    return ref, bias, smax
+
+
+def _tau_for(L, P, q, Ks, lengths, Wg):
+    """A tau that spreads the gates of group (0, 0) over a few units."""
+    G = L.Hq // L.Hkv
+    kind = 0 if L.desc_kind == MINMAX else 1
+    _, _, _, sc = O.decode_group(q[0, :G], Ks[0][0, :lengths[0]], Ks[0][0, :lengths[0]],
+                                 L.block, kind, W=Wg, budget_tokens=P.budget_tokens,
+                                 sparsity_bp=P.sparsity_bp, n_local=P.n_local, n_min=P.n_min,
+                                 want_scores=True)
+    fin = sc[np.isfinite(sc)]
+    sd = float(fin.std()) if fin.size > 1 else 1.0
+    return 3.0 / max(sd, 1e-3)
+
+
+@pytest.mark.parametrize("case", GATE_CASES, ids=[f"g{i}" for i in range(len(GATE_CASES))])
+def test_gated_select_decode_parity(case):
+    import torch
+    dtype, d, blk, kind, Hq, Hkv, lengths, budget, bp, nl, nm = case
+    B = len(lengths)
+    max_blocks = (max(lengths) + blk - 1) // blk + 2
+    L = bsa.Layout(B, Hq, Hkv, d, blk, max_blocks, dtype, kind)
+    P = bsa.SelectParams(budget_tokens=budget, sparsity_bp=bp, n_local=nl, n_min=nm)
+    P.n_max = bsa.block_count(P, max_blocks, blk)
+    q, Ks, Vs, Wg = make_inputs(31 + len(lengths), B, Hq, Hkv, d, lengths, dtype, kind)
+    enforce_gap(L, P, q, Ks, [[T] for T in lengths], W_gate=Wg)
+    tau = _tau_for(L, P, q, Ks, lengths, Wg)
+    print(f"case {case} tau {tau:.4g}", flush=True)
+    cache = bsa.allocate_cache(L, page_table=random_page_table(L, 9))
+    cache.k_pool.fill_(float("nan"))
+    cache.v_pool.fill_(float("nan"))
+    prefill(L, cache, Ks, Vs, lengths)
+    if Wg is not None:
+        P.gate_w = to_dev(Wg, bsa.Layout(1, 1, 1, d, blk, 1, BF16))
+    dev = "cuda"
+    idx = torch.full((B, Hkv, P.n_max), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device=dev)
+    P.gate_tau = tau
+    P.gate_bias = torch.full((B, Hkv, P.n_max), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(bsa.workspace_size(L, bsa.OP_SELECT, P.n_max),
+                         bsa.workspace_size(L, bsa.OP_DECODE, P.n_max)),
+                     dtype=torch.uint8, device=dev)
+    ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+    q_dev = to_dev(q, L)
+    bsa.select_blocks(L, cache, q_dev, P, idx, cnt, ws)
+    o = torch.full((B, Hq, d), float("nan"), dtype=q_dev.dtype, device=dev)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=dev)
+    bsa.sparse_decode_gated(L, cache, q_dev, idx, cnt, P.gate_bias, P.n_max, 1.0 / math.sqrt(d),
+                            o, lse, ws)
+    torch.cuda.synchronize()
+    ref, rbias, smax = _oracle_gated(L, P, q, Ks, Vs, lengths, tau, Wg)
+    compare_step(L, idx, cnt, o, lse, ref)
+    gb = P.gate_bias.cpu().numpy()
+    cn = cnt.cpu().numpy()
+    worst = 0.0
+    for (s, h), rb in rbias.items():
+        c = int(cn[s, h])
+        NC = max(0, -(-lengths[s] // blk) - nl)
+        tol = tau * 2e-5 * smax + 1e-4 + NC * 1.2e-7
+        err = np.abs(gb[s, h, :c] - rb).max() if c else 0.0
+        assert err <= tol, f"group {(s, h)}: bias err {err} > {tol}"
+        assert np.all(gb[s, h, c:] == 0.0)
+        worst = max(worst, err)
+    print(f"worst bias err {worst:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("dtype,d,blk", [(BF16, 128, 64), (BF16, 64, 128), (F32, 64, 32)])
+def test_gated_decode_with_arbitrary_bias(dtype, d, blk):
+    """The gated decode with a bias that no selection wrote (random values in
+    [-4, 1], random kept lists) equals the oracle's biased attention."""
+    import torch
+    lengths = [blk * 40 + 5, blk * 13]
+    Hq, Hkv = 8, 2
+    B = len(lengths)
+    max_blocks = (max(lengths) + blk - 1) // blk + 1
+    L = bsa.Layout(B, Hq, Hkv, d, blk, max_blocks, dtype, MINMAX)
+    q, Ks, Vs, _ = make_inputs(91, B, Hq, Hkv, d, lengths, dtype, MINMAX)
+    cache = bsa.allocate_cache(L, page_table=random_page_table(L, 4))
+    prefill(L, cache, Ks, Vs, lengths)
+    rng = np.random.Generator(np.random.PCG64(5))
+    n_max = max_blocks
+    idx = np.full((B, Hkv, n_max), -1, np.int32)
+    cnt = np.zeros((B, Hkv), np.int32)
+    bias = np.zeros((B, Hkv, n_max), np.float32)
+    for s, T in enumerate(lengths):
+        NB = -(-T // blk)
+        for h in range(Hkv):
+            k = int(rng.integers(1, NB + 1))
+            sel = np.sort(rng.choice(NB, size=k, replace=False)).astype(np.int32)
+            idx[s, h, :k] = sel
+            cnt[s, h] = k
+            bias[s, h, :k] = rng.uniform(-4, 1, k).astype(np.float32)
+    ws = torch.empty(bsa.workspace_size(L, bsa.OP_DECODE, n_max), dtype=torch.uint8,
+                     device="cuda")
+    q_dev = to_dev(q, L)
+    o = torch.full((B, Hq, d), float("nan"), dtype=q_dev.dtype, device="cuda")
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    bsa.sparse_decode_gated(L, cache, q_dev, torch.from_numpy(idx).cuda(),
+                            torch.from_numpy(cnt).cuda(), torch.from_numpy(bias).cuda(), n_max,
+                            0.1, o, lse, ws)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    o = o.float().cpu().numpy()
+    lse = lse.cpu().numpy()
+    worst_o = worst_l = 0.0
+    for s, T in enumerate(lengths):
+        for h in range(Hkv):
+            k = cnt[s, h]
+            for g in range(G):
+                ro, rl = O.attend_biased(q[s, h * G + g], Ks[s][h, :T], Vs[s][h, :T], blk,
+                                         idx[s, h, :k], bias[s, h, :k].astype(np.float64), 0.1)
+                worst_o = max(worst_o, float(np.abs(o[s, h * G + g] - ro).max()))
+                worst_l = max(worst_l, abs(lse[s, h * G + g] - rl) / max(1.0, abs(rl)))
+    assert worst_o <= 2e-2, worst_o
+    assert worst_l <= 1e-4, worst_l
+
+
+def test_gated_decode_constant_bias_is_shifted_plain_decode():
+    """A constant bias c on every kept block: o equals the ungated decode's
+    and lse moves by c (same kernels, same split)."""
+    import torch
+    d, blk, Hq, Hkv = 128, 64, 8, 2
+    lengths = [3000, 1234]
+    B = len(lengths)
+    max_blocks = (max(lengths) + blk - 1) // blk + 1
+    L = bsa.Layout(B, Hq, Hkv, d, blk, max_blocks, BF16, MINMAX)
+    P = bsa.SelectParams(sparsity_bp=8000, n_local=2, n_min=2)
+    P.n_max = bsa.block_count(P, max_blocks, blk)
+    q, Ks, Vs, _ = make_inputs(17, B, Hq, Hkv, d, lengths, BF16, MINMAX)
+    cache = bsa.allocate_cache(L, page_table=random_page_table(L, 2))
+    prefill(L, cache, Ks, Vs, lengths)
+    idx = torch.empty((B, Hkv, P.n_max), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((B, Hkv), dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(bsa.workspace_size(L, bsa.OP_SELECT, P.n_max),
+                         bsa.workspace_size(L, bsa.OP_DECODE, P.n_max)),
+                     dtype=torch.uint8, device="cuda")
+    q_dev = to_dev(q, L)
+    bsa.select_blocks(L, cache, q_dev, P, idx, cnt, ws)
+    outs = []
+    for c in (None, -1.5):
+        o = torch.empty((B, Hq, d), dtype=q_dev.dtype, device="cuda")
+        lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+        if c is None:
+            bsa.sparse_decode(L, cache, q_dev, idx, cnt, P.n_max, 0.09, o, lse, ws)
+        else:
+            bias = torch.full((B, Hkv, P.n_max), c, dtype=torch.float32, device="cuda")
+            bsa.sparse_decode_gated(L, cache, q_dev, idx, cnt, bias, P.n_max, 0.09, o, lse, ws)
+        torch.cuda.synchronize()
+        outs.append((o.float().cpu(), lse.cpu()))
+    assert (outs[0][0] - outs[1][0]).abs().max().item() <= 1e-2
+    assert ((outs[1][1] - (outs[0][1] - 1.5)).abs() / outs[0][1].abs().clamp(min=1)).max() <= 1e-5

@@ -569,3 +569,19 @@ def test_decode_group_gated_matches_selection_and_sdpa(kind):
         z = scale * (K.astype(np.float64) @ q[h].astype(np.float64)) + m
         np.testing.assert_allclose(o[h], o_ref, rtol=1e-10, atol=1e-12)
         assert abs(lse[h] - logsumexp(z)) < 1e-10
+
+
+def test_attend_biased_constant_bias_is_a_shift():
+    """One bias c on every kept block leaves o unchanged and moves lse by c
+    (so uniform gates reduce the gated step to the plain one, up to a
+    constant)."""
+    r = rng(66)
+    T, b, d = 450, 32, 8
+    K = r.standard_normal((T, d)).astype(np.float32)
+    V = r.standard_normal((T, d)).astype(np.float32)
+    q = r.standard_normal(d).astype(np.float32)
+    idx = np.array([1, 4, 6, 13, 14], np.int32)
+    o1, l1 = O.attend_biased(q, K, V, b, idx, np.full(5, -2.75), 0.3)
+    o2, l2 = O.attend(q, K, V, b, idx, 0.3)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    assert abs(l1 - (l2 - 2.75)) < 1e-12
