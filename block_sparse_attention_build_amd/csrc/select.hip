@@ -282,21 +282,27 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     int32_t* out = a.idx + static_cast<int64_t>(grp) * a.n_max;
     const float* sc = a.scores + static_cast<int64_t>(grp) * p.stride;
 
+    // Slots past the candidates hold the key 0, below every real key (the
+    // scores are never NaN, so the smallest real key, that of -inf, is
+    // 0x007fffff).  It never passes key > tau or key == tau (tau >= the
+    // smallest real key) and is skipped by the radix passes' key != 0 test,
+    // so no phase needs a per-key bounds test.
     const int base = tid * KPT;
     uint32_t key[KPT];
     if (KPT >= 4) {
         // branch-free 16-byte loads: the row is padded to a multiple of 4 and
-        // groups past the end read the row's first group (results unused)
+        // groups past the end read the row's first group
 #pragma unroll
         for (int r = 0; r < KPT; r += 4) {
             const int g0 = (base + r < NC) ? base + r : 0;
             const floatx4 v = *reinterpret_cast<const floatx4*>(sc + g0);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) key[r + k] = float_key(v[k]);
+            for (int k = 0; k < 4; ++k) key[r + k] = (base + r + k < NC) ? float_key(v[k]) : 0u;
         }
     } else {
 #pragma unroll
-        for (int r = 0; r < KPT; ++r) key[r] = float_key(sc[(base + r < NC) ? base + r : 0]);
+        for (int r = 0; r < KPT; ++r)
+            key[r] = (base + r < NC) ? float_key(sc[base + r]) : 0u;
     }
 
     // Log-gate bias ("Simple Attention Sparsification", Method): gates are
@@ -347,13 +353,12 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     uint32_t tau = 0;
     int need_eq = 0;
     if (mode == 2) {
+        // minimum of key - 1 (the sentinel wraps to the top), maximum of key
         uint32_t lmin = 0xffffffffu, lmax = 0u;
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
-            if (base + r < NC) {
-                lmin = min(lmin, key[r]);
-                lmax = max(lmax, key[r]);
-            }
+            lmin = min(lmin, key[r] - 1u);
+            lmax = max(lmax, key[r]);
         }
         lmin = wave_min_u32(lmin);
         lmax = wave_max_u32(lmax);
@@ -368,6 +373,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             kmin = min(kmin, red_min[w]);
             kmax = max(kmax, red_max[w]);
         }
+        kmin += 1u;
         const uint32_t range = kmax - kmin;
         uint32_t prefix = 0;  // of key - kmin, above the current digit
         int krem = K;
@@ -408,11 +414,9 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             for (int i = 0; i < 4; ++i) hw[lane + 64 * i] = 0;  // nobody reads it now
 #pragma unroll
             for (int r = 0; r < KPT; ++r) {
-                if (base + r < NC) {
-                    const uint32_t kr = key[r] - kmin;
-                    const bool alive = hi >= 32 || ((kr >> hi) == (prefix >> hi));
-                    if (alive) atomicAdd(&hw[(kr >> shift) & ((1u << dbits) - 1u)], 1);
-                }
+                const uint32_t kr = key[r] - kmin;
+                const bool alive = key[r] != 0u && (hi >= 32 || ((kr >> hi) == (prefix >> hi)));
+                if (alive) atomicAdd(&hw[(kr >> shift) & ((1u << dbits) - 1u)], 1);
             }
             if (tid == 0) n_alive_s = 0;  // for the alive-key list below
             __syncthreads();
@@ -441,10 +445,9 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             if (shift > 0 && n_alive <= kAliveCap) {
 #pragma unroll
                 for (int r = 0; r < KPT; ++r) {
-                    if (base + r < NC) {
-                        const uint32_t kr = key[r] - kmin;
-                        if ((kr >> shift) == (prefix >> shift)) alive_s[atomicAdd(&n_alive_s, 1)] = kr;
-                    }
+                    const uint32_t kr = key[r] - kmin;
+                    if (key[r] != 0u && (kr >> shift) == (prefix >> shift))
+                        alive_s[atomicAdd(&n_alive_s, 1)] = kr;
                 }
                 __syncthreads();
                 if (wave == 0) {
@@ -484,9 +487,8 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         int n_gt = 0, n_eq = 0;
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
-            const bool valid = base + r < NC;
-            n_gt += (valid && key[r] > tau) ? 1 : 0;
-            n_eq += (valid && key[r] == tau) ? 1 : 0;
+            n_gt += (key[r] > tau) ? 1 : 0;
+            n_eq += (key[r] == tau) ? 1 : 0;
         }
         const int packed = (n_gt << 16) | n_eq;
         const int incl = wave_incl_scan(packed);
@@ -500,11 +502,10 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         int pos = (excl >> 16) + min(eq_rank, need_eq);
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
-            const bool valid = base + r < NC;
             bool take = false;
-            if (valid && key[r] > tau) {
+            if (key[r] > tau) {
                 take = true;
-            } else if (valid && key[r] == tau) {
+            } else if (key[r] == tau) {
                 take = eq_rank < need_eq;
                 ++eq_rank;
             }
