@@ -483,14 +483,16 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         tau = kmin + prefix;
         need_eq = krem;
 
-        // one packed scan: (keys > tau) << 16 | (keys == tau), per thread
-        int n_gt = 0, n_eq = 0;
+        // one packed scan: (keys > tau) << 16 | (keys == tau), per thread;
+        // the positions of those keys are kept as bit masks
+        uint32_t gt_m = 0u, eq_m = 0u;
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
-            n_gt += (key[r] > tau) ? 1 : 0;
-            n_eq += (key[r] == tau) ? 1 : 0;
+            gt_m |= (key[r] > tau) ? (1u << r) : 0u;
+            eq_m |= (key[r] == tau) ? (1u << r) : 0u;
         }
-        const int packed = (n_gt << 16) | n_eq;
+        const int n_eq = __builtin_popcount(eq_m);
+        const int packed = (__builtin_popcount(gt_m) << 16) | n_eq;
         const int incl = wave_incl_scan(packed);
         if (lane == 63) wsum[wave] = incl;
         __syncthreads();
@@ -498,22 +500,33 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
 #pragma unroll
         for (int w = 0; w < kTopnWaves; ++w) before += (w < wave) ? wsum[w] : 0;
         const int excl = before + incl - packed;
-        int eq_rank = excl & 0xffff;
+        const int eq_rank = excl & 0xffff;
         int pos = (excl >> 16) + min(eq_rank, need_eq);
+        // this thread's keys equal to tau are ranked eq_rank, eq_rank + 1, ...
+        // (ascending index); those ranked below need_eq are taken
+        uint32_t take_m = gt_m;
+        for (int k = max(0, min(need_eq - eq_rank, n_eq)); k > 0; --k) {
+            take_m |= eq_m & (0u - eq_m);
+            eq_m &= eq_m - 1u;
+        }
+        if (bias_out) {
 #pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            bool take = false;
-            if (key[r] > tau) {
-                take = true;
-            } else if (key[r] == tau) {
-                take = eq_rank < need_eq;
-                ++eq_rank;
+            for (int r = 0; r < KPT; ++r) {
+                if ((take_m >> r) & 1u) {
+                    if (pos < a.n_max) {
+                        out[pos] = base + r;
+                        bias_out[pos] = gate(key[r]);
+                    }
+                    ++pos;
+                }
             }
-            if (take && pos < a.n_max) {
-                out[pos] = base + r;
-                if (bias_out) bias_out[pos] = gate(key[r]);
+        } else {
+            // only the taken keys, lowest index first
+            while (take_m != 0u) {
+                if (pos < a.n_max) out[pos] = base + __builtin_ctz(take_m);
+                ++pos;
+                take_m &= take_m - 1u;
             }
-            pos += take ? 1 : 0;
         }
     }
     const int picked = (mode == 0) ? 0 : K;
