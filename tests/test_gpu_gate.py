@@ -28,6 +28,9 @@ GATE_CASES = [
     (BF16, 64, 32, MINMAX, 4, 4, [777, 1025, 64, 65], 0, 8000, 1, 3),
     (F32, 64, 64, MINMAX, 4, 1, [2049], 512, 0, 1, 2),
     (F32, 128, 128, MEAN, 8, 2, [1500, 700], 0, 9000, 2, 0),
+    # mid-size rows (about 1900 and 3100 candidates)
+    (BF16, 64, 32, MINMAX, 4, 1, [60000], 0, 9000, 1, 2),
+    (BF16, 64, 32, MINMAX, 8, 2, [98000, 40000], 0, 9500, 2, 4),
 ]
 
 
