@@ -182,6 +182,26 @@ def test_select_decode_parity(case):
         assert eo <= 1e-4, eo  # fp32 I/O diagnostic bar
 
 
+def test_select_decode_at_the_longest_row():
+    """The longest row the top-n accepts: max_blocks = 32768 (32 keys per
+    thread), one sequence of about 1M tokens at b = 32 with a partial last
+    block, p = 0.9 (3277 kept blocks, 256 splits)."""
+    d, blk, Hq, Hkv = 64, 32, 4, 1
+    max_blocks = 32768
+    T = max_blocks * blk - 40
+    L = bsa.Layout(1, Hq, Hkv, d, blk, max_blocks, BF16, MINMAX)
+    P = bsa.SelectParams(sparsity_bp=9000, n_local=2, n_min=16)
+    P.n_max = bsa.block_count(P, max_blocks, blk)
+    q, Ks, Vs, _ = make_inputs(202, 1, Hq, Hkv, d, [T], BF16, MINMAX)
+    enforce_gap(L, P, q, Ks, [[T]])
+    cache = bsa.allocate_cache(L, page_table=random_page_table(L, 6))
+    prefill(L, cache, Ks, Vs, [T])
+    idx, cnt, o, lse = run_select_decode(L, cache, to_dev(q, L), P)
+    ref = oracle_decode(P, q, Ks, Vs, [T], L)
+    compare_step(L, idx, cnt, o, lse, ref)
+    assert int(cnt[0, 0]) == P.n_max
+
+
 @pytest.mark.parametrize("dtype,d,blk,kind", [(BF16, 128, 64, MINMAX), (BF16, 64, 128, MEAN),
                                               (F32, 64, 32, MINMAX)])
 def test_append_select_equals_the_two_calls(dtype, d, blk, kind):
