@@ -349,13 +349,28 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     }
     __syncthreads();
 
-    // merge of the units, in unit order, into one partial per head
+    // merge of the units, in unit order, into one partial per head: the
+    // per-head maximum and every unit's weight 2^(m_u - M) are formed once
+    // (the weights overwrite um), then each output channel sums over the
+    // units with several LDS reads in flight
+    __shared__ float s_M[16];
+    if (threadIdx.x < 16) {
+        float M = -INFINITY;
+#pragma unroll 8
+        for (int u = 0; u < n_units; ++u) M = fmaxf(M, um[u * 16 + threadIdx.x]);
+        s_M[threadIdx.x] = M;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n_units * 16; i += kDecThreads) {
+        const float M = s_M[i & 15];
+        um[i] = (M == -INFINITY) ? 0.f : exp2f(um[i] - M);
+    }
+    __syncthreads();
     const int64_t head_row0 = static_cast<int64_t>(s) * c.Hq + kvh * G;
     for (int k = threadIdx.x; k < G * D; k += kDecThreads) {
         const int h = k / D;
         const int ch = k - h * D;
-        float M = -INFINITY;
-        for (int u = 0; u < n_units; ++u) M = fmaxf(M, um[u * 16 + h]);
+        const float M = s_M[h];
         const int64_t row = head_row0 + h;
         float* op = a.o_part + (row * S + split) * D;
         if (M == -INFINITY) {
@@ -364,8 +379,9 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
             continue;
         }
         float L = 0.f, acc = 0.f;
+#pragma unroll 8
         for (int u = 0; u < n_units; ++u) {
-            const float sc = exp2f(um[u * 16 + h] - M);
+            const float sc = um[u * 16 + h];
             L += ul[u * 16 + h] * sc;
             acc += uo[(u * G + h) * D + ch] * sc;
         }
