@@ -202,7 +202,8 @@ BSA_API bsa_status bsa_build_block_desc(const bsa_layout* layout, const bsa_cach
  * computed in fp32.
  * q: [B][Hq][d] in the KV dtype.
  * idx: [B][Hkv][n_max] int32, OUT: kept block ids ascending, padded with -1.
- * cnt: [B][Hkv] int32, OUT: n.
+ * cnt: [B][Hkv] int32, OUT: n.  An empty sequence (seq_lens[s] = 0) has no
+ *   block: cnt = 0 and its idx rows are all -1.
  * ws: workspace of at least bsa_workspace_size(layout, BSA_OP_SELECT, n_max)
  *   bytes (holds the scores; contents need no initialisation).
  * gate_bias (optional): see bsa_select_params.
@@ -244,7 +245,8 @@ BSA_API bsa_status bsa_append_select(const bsa_layout* layout, const bsa_cache* 
  *   lse_h = ln sum_t exp(z_t), t over the kept blocks' tokens (< seq_lens).
  * q: [B][Hq][d]; idx/cnt: as written by bsa_select_blocks with row length
  * n_max (any ascending or not, duplicate-free list of valid block ids works).
- * o: [B][Hq][d] in the KV dtype, OUT.  lse: [B][Hq] fp32, OUT.
+ * o: [B][Hq][d] in the KV dtype, OUT.  lse: [B][Hq] fp32, OUT.  A group with
+ *   cnt = 0 (e.g. an empty sequence) attends to nothing: o = 0, lse = -inf.
  * ws: at least bsa_workspace_size(layout, BSA_OP_DECODE, n_max) bytes.
  * Errors: BSA_ERR_NULL, BSA_ERR_SHAPE, BSA_ERR_UNSUPPORTED, BSA_ERR_PARAM
  *   (n_max < 1, softmax_scale not finite and > 0), BSA_ERR_WORKSPACE,

@@ -430,3 +430,65 @@ def test_rectify_parity(dtype, d, blk, f, lengths, Hq, Hkv):
 def torch_dtype_of(L):
     torch = _torch()
     return torch.bfloat16 if L.kv_dtype == BF16 else torch.float32
+
+
+@pytest.mark.parametrize("dtype,gated", [(BF16, False), (BF16, True), (F32, False)])
+def test_empty_sequences_in_a_ragged_batch(dtype, gated):
+    """Sequences with seq_lens = 0 next to non-empty ones: the empty groups
+    keep no block (cnt 0, idx all -1, bias 0) and attend to nothing (o = 0,
+    lse = -inf, as documented); the others equal the oracle."""
+    torch = _torch()
+    d, blk, Hq, Hkv = 64, 64, 8, 2
+    lengths = [0, 700, 0, 65]
+    B = len(lengths)
+    max_blocks = 14
+    L = bsa.Layout(B, Hq, Hkv, d, blk, max_blocks, dtype, MINMAX)
+    P = bsa.SelectParams(sparsity_bp=8000, n_local=1, n_min=2)
+    P.n_max = bsa.block_count(P, max_blocks, blk)
+    q, Ks, Vs, _ = make_inputs(303, B, Hq, Hkv, d, lengths, dtype, MINMAX)
+    enforce_gap(L, P, q, Ks, [[T] for T in lengths])
+    cache = bsa.allocate_cache(L, page_table=random_page_table(L, 7))
+    prefill(L, cache, Ks, Vs, lengths)
+    cache.seq_lens.copy_(torch.tensor(lengths, dtype=torch.int32, device="cuda"))
+    q_dev = to_dev(q, L)
+    idx = torch.full((B, Hkv, P.n_max), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((B, Hkv), -7, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(bsa.workspace_size(L, bsa.OP_SELECT, P.n_max),
+                         bsa.workspace_size(L, bsa.OP_DECODE, P.n_max)),
+                     dtype=torch.uint8, device="cuda")
+    ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+    if gated:
+        P.gate_tau = 0.01
+        P.gate_bias = torch.full((B, Hkv, P.n_max), float("nan"), dtype=torch.float32,
+                                 device="cuda")
+    bsa.select_blocks(L, cache, q_dev, P, idx, cnt, ws)
+    o = torch.full((B, Hq, d), float("nan"), dtype=q_dev.dtype, device="cuda")
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device="cuda")
+    if gated:
+        bsa.sparse_decode_gated(L, cache, q_dev, idx, cnt, P.gate_bias, P.n_max,
+                                1 / math.sqrt(d), o, lse, ws)
+    else:
+        bsa.sparse_decode(L, cache, q_dev, idx, cnt, P.n_max, 1 / math.sqrt(d), o, lse, ws)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    for s in (0, 2):
+        assert cnt[s].tolist() == [0, 0]
+        assert torch.all(idx[s] == -1)
+        assert torch.all(o[s] == 0)
+        assert torch.all(torch.isneginf(lse[s]))
+        if gated:
+            assert torch.all(P.gate_bias[s] == 0)
+    live = [1, 3]
+    if gated:
+        ref = {}
+        for s in live:
+            for h in range(Hkv):
+                r_idx, r_o, r_lse, _ = O.decode_group_gated(
+                    q[s, h * G:(h + 1) * G], Ks[s][h, :lengths[s]], Vs[s][h, :lengths[s]], blk,
+                    0, 0.01, sparsity_bp=8000, n_local=1, n_min=2, scale=1 / math.sqrt(d))
+                ref[(s, h)] = (r_idx, r_o, r_lse)
+    else:
+        ref = oracle_decode(P, q[live], [Ks[s] for s in live], [Vs[s] for s in live],
+                            [lengths[s] for s in live], L)
+        ref = {(live[s], h): v for (s, h), v in ref.items()}
+    compare_step(L, idx, cnt, o, lse, ref)
