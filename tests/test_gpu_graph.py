@@ -1,6 +1,8 @@
-"""The four entry points captured into one HIP graph: every replay must
-equal the eager result of the same inputs (the library records no memset
-nodes; replays are interleaved with eager work and synchronisations)."""
+"""The entry points captured into one HIP graph: every replay must equal the
+eager result of the same inputs (the library records no memset nodes;
+replays are interleaved with eager work and synchronisations).  Two step
+forms: the separate calls, and the fused append + select writing the
+log-gate bias with the gated decode."""
 import math
 
 import numpy as np
@@ -13,7 +15,8 @@ from test_gpu_parity import make_inputs
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("form", ["separate", "fused_gated"])
+def test_graph_replays_match_eager(form):
     import torch
     d, blk, f = 128, 64, 32
     lengths = [3000, 1777]
@@ -43,15 +46,23 @@ def test_graph_replays_match_eager():
                     lse=torch.zeros(2, 8, dtype=torch.float32, device=dev),
                     o_r=torch.zeros(2, 8, f, d, dtype=torch.bfloat16, device=dev),
                     lse_r=torch.zeros(2, 8, f, dtype=torch.float32, device=dev),
+                    bias=torch.zeros(2, 2, P.n_max, dtype=torch.float32, device=dev),
                     ws=torch.zeros(ws_bytes, dtype=torch.uint8, device=dev))
         return cache, bufs
 
     def step(cache, b):
         cache.seq_lens.add_(1)
-        bsa.build_block_desc(L, cache, kn, vn, 1)
-        bsa.select_blocks(L, cache, qd, P, b["idx"], b["cnt"], b["ws"])
-        bsa.sparse_decode(L, cache, qd, b["idx"], b["cnt"], P.n_max, 1 / math.sqrt(d), b["o"],
-                          b["lse"], b["ws"])
+        if form == "separate":
+            bsa.build_block_desc(L, cache, kn, vn, 1)
+            bsa.select_blocks(L, cache, qd, P, b["idx"], b["cnt"], b["ws"])
+            bsa.sparse_decode(L, cache, qd, b["idx"], b["cnt"], P.n_max, 1 / math.sqrt(d), b["o"],
+                              b["lse"], b["ws"])
+        else:
+            Pg = bsa.SelectParams(sparsity_bp=8000, n_local=2, n_min=4, n_max=P.n_max,
+                                  gate_tau=0.02, gate_bias=b["bias"])
+            bsa.append_select(L, cache, kn, vn, qd, Pg, b["idx"], b["cnt"], b["ws"])
+            bsa.sparse_decode_gated(L, cache, qd, b["idx"], b["cnt"], b["bias"], P.n_max,
+                                    1 / math.sqrt(d), b["o"], b["lse"], b["ws"])
         bsa.rectify_chunk(L, cache, qr, kr, vr, f, 1 / math.sqrt(d), b["o_r"], b["lse_r"], b["ws"])
 
     # eager reference: three consecutive steps from the same start
