@@ -287,22 +287,30 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     // 0x007fffff).  It never passes key > tau or key == tau (tau >= the
     // smallest real key) and is skipped by the radix passes' key != 0 test,
     // so no phase needs a per-key bounds test.
+    // A wave whose first slot is past the candidates holds only the key 0
+    // (KPT is sized for the capacity, the row for the current length): such
+    // a wave skips every per-key loop below but takes part in every barrier.
     const int base = tid * KPT;
+    const bool live = wave * kWave * KPT < NC;  // wave-uniform
     uint32_t key[KPT];
-    if (KPT >= 4) {
-        // branch-free 16-byte loads: the row is padded to a multiple of 4 and
-        // groups past the end read the row's first group
 #pragma unroll
-        for (int r = 0; r < KPT; r += 4) {
-            const int g0 = (base + r < NC) ? base + r : 0;
-            const floatx4 v = *reinterpret_cast<const floatx4*>(sc + g0);
+    for (int r = 0; r < KPT; ++r) key[r] = 0u;
+    if (live) {
+        if (KPT >= 4) {
+            // branch-free 16-byte loads: the row is padded to a multiple of 4
+            // and groups past the end read the row's first group
 #pragma unroll
-            for (int k = 0; k < 4; ++k) key[r + k] = (base + r + k < NC) ? float_key(v[k]) : 0u;
+            for (int r = 0; r < KPT; r += 4) {
+                const int g0 = (base + r < NC) ? base + r : 0;
+                const floatx4 v = *reinterpret_cast<const floatx4*>(sc + g0);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) key[r + k] = (base + r + k < NC) ? float_key(v[k]) : 0u;
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < KPT; ++r)
+                key[r] = (base + r < NC) ? float_key(sc[base + r]) : 0u;
         }
-    } else {
-#pragma unroll
-        for (int r = 0; r < KPT; ++r)
-            key[r] = (base + r < NC) ? float_key(sc[base + r]) : 0u;
     }
 
     // Log-gate bias ("Simple Attention Sparsification", Method): gates are
@@ -313,9 +321,11 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     float g_smax = 0.f, g_lnz = 0.f;
     if (bias_out && NC > 0) {
         uint32_t lmax = 0u;
+        if (live) {
 #pragma unroll
-        for (int r = 0; r < KPT; ++r)
-            if (base + r < NC) lmax = max(lmax, key[r]);
+            for (int r = 0; r < KPT; ++r)
+                if (base + r < NC) lmax = max(lmax, key[r]);
+        }
         lmax = wave_max_u32(lmax);
         if (lane == 0) red_max[wave] = lmax;
         __syncthreads();
@@ -324,9 +334,11 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         for (int w = 0; w < kTopnWaves; ++w) kmx = max(kmx, red_max[w]);
         g_smax = key_float(kmx);
         float z = 0.f;
+        if (live) {
 #pragma unroll
-        for (int r = 0; r < KPT; ++r)
-            if (base + r < NC) z += expf(a.gate_tau * (key_float(key[r]) - g_smax));
+            for (int r = 0; r < KPT; ++r)
+                if (base + r < NC) z += expf(a.gate_tau * (key_float(key[r]) - g_smax));
+        }
         z = wave_sum(z);
         if (lane == 0) red_z[wave] = z;
         __syncthreads();
@@ -341,7 +353,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
 
     // mode: 0 = pick none, 1 = pick every candidate, 2 = threshold select
     const int mode = (K <= 0) ? 0 : (K >= NC ? 1 : 2);
-    if (mode == 1) {
+    if (mode == 1 && live) {
 #pragma unroll
         for (int r = 0; r < KPT; ++r) {
             if (base + r < NC) {
@@ -355,10 +367,12 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     if (mode == 2) {
         // minimum of key - 1 (the sentinel wraps to the top), maximum of key
         uint32_t lmin = 0xffffffffu, lmax = 0u;
+        if (live) {
 #pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            lmin = min(lmin, key[r] - 1u);
-            lmax = max(lmax, key[r]);
+            for (int r = 0; r < KPT; ++r) {
+                lmin = min(lmin, key[r] - 1u);
+                lmax = max(lmax, key[r]);
+            }
         }
         lmin = wave_min_u32(lmin);
         lmax = wave_max_u32(lmax);
@@ -412,11 +426,13 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             int* hw = hist[wave];
 #pragma unroll
             for (int i = 0; i < 4; ++i) hw[lane + 64 * i] = 0;  // nobody reads it now
+            if (live) {
 #pragma unroll
-            for (int r = 0; r < KPT; ++r) {
-                const uint32_t kr = key[r] - kmin;
-                const bool alive = key[r] != 0u && (hi >= 32 || ((kr >> hi) == (prefix >> hi)));
-                if (alive) atomicAdd(&hw[(kr >> shift) & ((1u << dbits) - 1u)], 1);
+                for (int r = 0; r < KPT; ++r) {
+                    const uint32_t kr = key[r] - kmin;
+                    const bool alive = key[r] != 0u && (hi >= 32 || ((kr >> hi) == (prefix >> hi)));
+                    if (alive) atomicAdd(&hw[(kr >> shift) & ((1u << dbits) - 1u)], 1);
+                }
             }
             if (tid == 0) n_alive_s = 0;  // for the alive-key list below
             __syncthreads();
@@ -443,11 +459,24 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             const int d1 = block_pass();
             const int n_alive = hsum[d1];
             if (shift > 0 && n_alive <= kAliveCap) {
+                // list slots: a lane mask of the alive keys, a wave prefix of
+                // the lane counts and one LDS atomic per wave for its base
+                if (live) {
+                    uint32_t am = 0u;
 #pragma unroll
-                for (int r = 0; r < KPT; ++r) {
-                    const uint32_t kr = key[r] - kmin;
-                    if (key[r] != 0u && (kr >> shift) == (prefix >> shift))
-                        alive_s[atomicAdd(&n_alive_s, 1)] = kr;
+                    for (int r = 0; r < KPT; ++r) {
+                        const uint32_t kr = key[r] - kmin;
+                        am |= (key[r] != 0u && (kr >> shift) == (prefix >> shift)) ? (1u << r) : 0u;
+                    }
+                    const int cnt_l = __builtin_popcount(am);
+                    const int incl = wave_incl_scan(cnt_l);
+                    int wbase = 0;
+                    if (lane == 63) wbase = atomicAdd(&n_alive_s, incl);
+                    int at = __builtin_amdgcn_readlane(wbase, 63) + incl - cnt_l;
+#pragma unroll
+                    for (int r = 0; r < KPT; ++r) {
+                        if (am & (1u << r)) alive_s[at++] = key[r] - kmin;
+                    }
                 }
                 __syncthreads();
                 if (wave == 0) {
@@ -486,10 +515,12 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         // one packed scan: (keys > tau) << 16 | (keys == tau), per thread;
         // the positions of those keys are kept as bit masks
         uint32_t gt_m = 0u, eq_m = 0u;
+        if (live) {
 #pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            gt_m |= (key[r] > tau) ? (1u << r) : 0u;
-            eq_m |= (key[r] == tau) ? (1u << r) : 0u;
+            for (int r = 0; r < KPT; ++r) {
+                gt_m |= (key[r] > tau) ? (1u << r) : 0u;
+                eq_m |= (key[r] == tau) ? (1u << r) : 0u;
+            }
         }
         const int n_eq = __builtin_popcount(eq_m);
         const int packed = (__builtin_popcount(gt_m) << 16) | n_eq;
@@ -509,7 +540,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             take_m |= eq_m & (0u - eq_m);
             eq_m &= eq_m - 1u;
         }
-        if (bias_out) {
+        if (bias_out && live) {
 #pragma unroll
             for (int r = 0; r < KPT; ++r) {
                 if ((take_m >> r) & 1u) {
