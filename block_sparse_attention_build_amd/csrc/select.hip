@@ -30,7 +30,13 @@
 //   finishes the search on it.  The kept blocks are then compacted in
 //   ascending index order with one block-wide prefix scan (ties at the
 //   threshold go to the lower index), the local blocks appended and the row
-//   padded with -1.
+//   padded with -1.  Keys per thread are sized for the capacity; slots past
+//   the row's candidates hold the key 0 (below every real key), and waves
+//   holding only such keys skip the per-key work.  With a gate-bias output
+//   ("Simple Attention Sparsification", Method: softmax gates over the
+//   candidate blocks, log g added to a kept block's logits) the kernel also
+//   forms the softmax normaliser over all candidates and writes each kept
+//   block's log-gate beside its id.
 #include "bsa_device.h"
 #include "bsa_internal.h"
 #include "kv_write_block.h"
