@@ -45,7 +45,10 @@ namespace bsa {
 
 namespace {
 
-constexpr int kScoreThreads = 256;
+#ifndef BSA_SCORE_THREADS
+#define BSA_SCORE_THREADS 256
+#endif
+constexpr int kScoreThreads = BSA_SCORE_THREADS;
 #ifndef BSA_SCORE_ITERS
 #define BSA_SCORE_ITERS 8
 #endif
