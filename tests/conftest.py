@@ -18,8 +18,8 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are skipped (not failed) where no GPU is visible, so that a
-    # plain `pytest` on a CPU-only machine stays green; `-m gpu` on a GPU machine
-    # runs them.
+    # plain `pytest` on a CPU-only machine stays green; `-m gpu` on a machine
+    # with an MI355X runs them.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
