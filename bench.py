@@ -86,7 +86,7 @@ def parse():
     ap.add_argument("--sparsity-bp", type=int, default=None)
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=40)
+    ap.add_argument("--cpu-steps", type=int, default=120)
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads (sparsity sweep, 32K, batched, ReSA loop)")
     ap.add_argument("--gate-tau", type=float, default=None,
