@@ -77,6 +77,41 @@ def measured_traffic(workload, bp):
     return int(t.group(1))
 
 
+def read_ceiling(dev):
+    """The device's streaming-read rate: the best of a few grid sizes of a
+    plain 16-byte streaming read over 4 GiB (libbsa_probe.so), timed with
+    HIP events on the current stream."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_build_amd", "libbsa_probe.so"))
+    lib.bsa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.bsa_probe_read.restype = ctypes.c_int
+    nbytes, grids = 4 << 30, (8192, 16384, 32768, 65536)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    sink = torch.empty(max(grids) * 256 * 16, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best, best_g = 0.0, 0
+    for g in grids:
+        for _ in range(3):
+            e0.record()
+            rc = lib.bsa_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), g, stream.cuda_stream)
+            e1.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError(f"bsa_probe_read failed ({rc})")
+            gbps = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            if gbps > best:
+                best, best_g = gbps, g
+    del buf, sink
+    torch.cuda.empty_cache()
+    return {"GBps": round(best, 1), "workgroups": best_g,
+            "probe": "streaming read of 4 GiB, 16-byte loads, grid-stride, best of 8192-65536 "
+                     "workgroups x 3 (libbsa_probe.so)"}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -417,13 +452,30 @@ def cpu_baseline(run, steps):
             list(ex.map(lambda h: one(step, h), range(w.Hkv)))
     el = time.time() - t
     us = el * 1e6 / steps * w.B
+    # the same work on one core, over an eighth of the steps
+    steps1 = max(1, steps // 8)
+    t = time.time()
+    for step in range(steps1):
+        for h in range(w.Hkv):
+            one(step, h)
+    el1 = time.time() - t
+    us1 = el1 * 1e6 / steps1 * w.B
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     a, b = step_bytes(run, [t + 1 for t in run.T0])
     return {"value": round((a + b) / (us * 1e-6) / 1e9, 4), "unit": "GB/s",
             "us_per_step_layer": round(us, 1), "cores": cores, "kind": "oracle",
             "sample": f"{steps} decode steps of layer 0, sequence 0, all {w.Hkv} KV-head groups at "
                       f"{T0}+ tokens (fp64 scalar C oracle, one thread per group); "
                       f"scaled by the batch size {w.B}",
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2),
+            "one_core": {"us_per_step_layer": round(us1, 1), "steps": steps1,
+                         "seconds": round(el1, 2)},
+            "cpu_model": model, "host_cpus": os.cpu_count()}
 
 
 def main():
@@ -500,6 +552,10 @@ def main():
         out["cpu_baseline"] = cpu_baseline(run, args.cpu_steps)
     del run
     torch.cuda.empty_cache()
+    ceil = read_ceiling(dev)
+    out["read_ceiling"] = ceil
+    out["pct_of_read_ceiling"] = round(100.0 * out["value"] / ceil["GBps"], 2)
+    out["roofline"]["frac_of_read_ceiling"] = round(out["roofline"]["achieved"] / ceil["GBps"], 4)
     if not args.headline_only:
         for name in ["qwen3_4b_32k", "batched_64k_gate", "resa_ragged"]:
             wx = W.get(name)

@@ -1,8 +1,9 @@
 """Build libbsa.so (the HIP kernels + C ABI) for gfx950 with hipcc.
 
-Every .hip file under csrc/ is compiled to an object in parallel, then linked
-into block_sparse_attention_build_amd/libbsa.so.  Objects go to _build/ at the
-repository root.
+Every .hip file directly under csrc/ is compiled to an object in parallel,
+then linked into block_sparse_attention_build_amd/libbsa.so.  The benchmark's
+read-bandwidth probe (csrc/probe/) is linked on its own into libbsa_probe.so.
+Objects go to _build/ at the repository root.
 """
 import concurrent.futures as cf
 import glob
@@ -14,6 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
+PROBE_LIB = os.path.join(PKG, "libbsa_probe.so")
 ARCH = "gfx950"
 
 CXXFLAGS = [
@@ -42,17 +44,23 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose):
+    tmp = lib + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probe = sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + probe))
+    _link(objs[:len(srcs)], LIB, verbose)
+    _link(objs[len(srcs):], PROBE_LIB, verbose)
     return LIB
 
 
