@@ -182,6 +182,24 @@ def test_fullsize_decode_step(name, sampled):
     select_decode_and_check(F, P, F.workspace())
 
 
+def test_split_cap_decides_the_split_count():
+    """256 groups (32 sequences x 8 KV heads) leave one split per group by the
+    workgroup target, but a split covers at most 4096 kept blocks (its block
+    and page ids are staged in LDS): 4400 kept blocks per group therefore run
+    as two splits.  Ragged contexts of 150K-181K tokens, b = 32, d = 64,
+    G = 8, token budget 140800 (4400 blocks)."""
+    w = W.Workload("split_cap", 90, B=32, Hq=64, Hkv=8, d=64, dtype="bf16",
+                   T0=tuple(150000 + 1000 * i for i in range(32)), block=32,
+                   budget_tokens=4400 * 32, n_local=2, n_min=0)
+    F = Filled(w, w.T0, [(0, 3), (17, 0), (31, 7)], 1090)
+    P = F.params[w.sparsity_bp]
+    assert P.n_max == 4400
+    F.enforce([P], [T + 1 for T in F.T])
+    F.allocate_and_prefill()
+    F.append_one()
+    select_decode_and_check(F, P, F.workspace())
+
+
 def test_fullsize_512k_sparsity_sweep():
     w = W.get("long_512k")
     sweep = [w.sparsity_bp] + [b for b in w.sparsity_sweep if b != w.sparsity_bp]

@@ -155,6 +155,12 @@ CASES = [
     # mid-size rows (about 1900 and 3100 candidates)
     (BF16, 64, 32, MINMAX, 4, 1, [60000], 0, 9000, 1, 2),
     (BF16, 64, 32, MINMAX, 8, 2, [98000, 40000], 0, 9500, 2, 4),
+    # groups of 3, 5 and 7 query heads (operand columns past G stay empty)
+    (BF16, 128, 64, MINMAX, 6, 2, [3100, 777], 0, 9000, 2, 3),
+    (BF16, 64, 32, MEAN, 10, 2, [1200, 2500], 256, 0, 1, 0),
+    (F32, 64, 64, MINMAX, 7, 1, [1500], 0, 8500, 1, 2),
+    # 33 x 8 = 264 groups: one split per group, so the merge kernel sees S = 1
+    (BF16, 64, 64, MINMAX, 16, 8, [100 + 97 * i for i in range(33)], 512, 0, 1, 2),
 ]
 
 
