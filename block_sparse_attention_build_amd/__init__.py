@@ -13,10 +13,14 @@ from dataclasses import dataclass
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-_LIBPATH = os.path.join(_PKG, "libbsa.so")
+LIB_DEFAULT = os.path.join(_PKG, "libbsa.so")
+# the build that verifies device-side contracts on the host (synchronises)
+LIB_CHECKED = os.path.join(_PKG, "libbsa_checked.so")
+_LIBPATH = LIB_CHECKED if os.environ.get("BSA_CHECKED") == "1" else LIB_DEFAULT
 
 # status codes (bsa_status)
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_PARAM, ERR_WORKSPACE, ERR_HIP = range(7)
+(OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_PARAM, ERR_WORKSPACE, ERR_HIP,
+ ERR_CONTRACT) = range(8)
 DTYPE_F32, DTYPE_BF16 = 0, 1
 DESC_MINMAX, DESC_MEANPOOL = 0, 1
 OP_SELECT, OP_DECODE, OP_RECTIFY = 1, 2, 3
@@ -59,7 +63,7 @@ def lib():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIBPATH):
-        raise RuntimeError(f"libbsa.so not found at {_LIBPATH}: build it first "
+        raise RuntimeError(f"{os.path.basename(_LIBPATH)} not found at {_LIBPATH}: build it first "
                            "(python -c 'import __graft_entry__ as g; g.build()')")
     L = ctypes.CDLL(_LIBPATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
@@ -82,6 +86,16 @@ def lib():
         fn.restype = ctypes.c_int
     _lib = L
     return L
+
+
+def use_library(path):
+    """Switch every binding to the library at path (LIB_DEFAULT or
+    LIB_CHECKED); returns the path in use before."""
+    global _lib, _LIBPATH
+    before = _LIBPATH
+    _lib, _LIBPATH = None, path
+    lib()
+    return before
 
 
 def status_string(status):

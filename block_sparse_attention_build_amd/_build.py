@@ -1,9 +1,12 @@
 """Build libbsa.so (the HIP kernels + C ABI) for gfx950 with hipcc.
 
 Every .hip file directly under csrc/ is compiled to an object in parallel,
-then linked into block_sparse_attention_build_amd/libbsa.so.  The benchmark's
-read-bandwidth probe (csrc/probe/) is linked on its own into libbsa_probe.so.
-Objects go to _build/ at the repository root.
+then linked into block_sparse_attention_build_amd/libbsa.so.  The C ABI
+layer (bsa_abi.hip) is compiled a second time with BSA_CHECKED=1 and linked
+with the same kernel objects into libbsa_checked.so, the build that verifies
+device-side contracts on the host.  The benchmark's read-bandwidth probe
+(csrc/probe/) is linked on its own into libbsa_probe.so.  Objects go to
+_build/ at the repository root.
 """
 import concurrent.futures as cf
 import glob
@@ -15,6 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbsa.so")
+CHECKED_LIB = os.path.join(PKG, "libbsa_checked.so")
+ABI_SRC = "bsa_abi.hip"
 PROBE_LIB = os.path.join(PKG, "libbsa_probe.so")
 ARCH = "gfx950"
 
@@ -28,9 +33,10 @@ CXXFLAGS = [
 ]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = ["hipcc", *CXXFLAGS, "-c", src, "-o", obj]
+def _compile(src, verbose, defines=()):
+    tag = "".join("." + d.split("=")[0].lower() for d in defines)
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
+    cmd = ["hipcc", *CXXFLAGS, *(f"-D{d}" for d in defines), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -57,10 +63,15 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     probe = sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + probe))
-    _link(objs[:len(srcs)], LIB, verbose)
-    _link(objs[len(srcs):], PROBE_LIB, verbose)
+    abi = os.path.join(CSRC, ABI_SRC)
+    jobs = [(src, ()) for src in srcs + probe] + [(abi, ("BSA_CHECKED=1",))]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    lib_objs = objs[:len(srcs)]
+    _link(lib_objs, LIB, verbose)
+    kernels = [o for o, src in zip(lib_objs, srcs) if os.path.basename(src) != ABI_SRC]
+    _link(kernels + [objs[-1]], CHECKED_LIB, verbose)
+    _link(objs[len(srcs):len(srcs) + len(probe)], PROBE_LIB, verbose)
     return LIB
 
 

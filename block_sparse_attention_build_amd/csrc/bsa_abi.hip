@@ -2,8 +2,22 @@
 // Every entry point validates its arguments on the host before any HIP call,
 // carves its workspace, enqueues its kernels on the caller's stream and
 // returns; nothing is allocated, nothing is synchronised.
+//
+// Built with BSA_CHECKED=1 (libbsa_checked.so), every entry point also
+// verifies the device-side contracts it states before enqueuing anything:
+// it drains the stream, copies the values the contracts bound (sequence
+// lengths, page ids in use, kept counts and ids, biases) to the host and
+// returns BSA_ERR_CONTRACT if one is broken.  That build synchronises on
+// every call, so it is for debugging, not for graph capture.
 #include <math.h>
 #include <stddef.h>
+
+#ifndef BSA_CHECKED
+#define BSA_CHECKED 0
+#endif
+#if BSA_CHECKED
+#include <vector>
+#endif
 
 #include "../../include/bsa.h"
 #include "bsa_device.h"
@@ -107,6 +121,82 @@ bsa_status check_select_params(const bsa_layout* L, const bsa_select_params* P) 
 
 bsa_status hip_status(hipError_t e) { return e == hipSuccess ? BSA_OK : BSA_ERR_HIP; }
 
+// ---------------------------------------------------------------------------
+// Device-side contracts, verified on the host (checked builds).  Each check
+// returns BSA_OK at once in the default build.
+// ---------------------------------------------------------------------------
+#if BSA_CHECKED
+// n elements at src, after the work already enqueued on the stream
+template <typename T>
+bool fetch(std::vector<T>& dst, const void* src, size_t n, hipStream_t stream) {
+    dst.assign(n, T());
+    if (n == 0) return true;
+    if (hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, stream) !=
+        hipSuccess)
+        return false;
+    return hipStreamSynchronize(stream) == hipSuccess;
+}
+
+int blocks_of(int32_t T, int block) { return (T + block - 1) / block; }
+#endif
+
+// lo <= seq_lens[s] <= max_blocks*block for every sequence, and a
+// non-negative page id for every block that holds tokens.  T_out (checked
+// builds) receives the lengths.
+#if BSA_CHECKED
+bsa_status contract_cache(const CacheArgs& c, int64_t lo, hipStream_t stream,
+                          std::vector<int32_t>* T_out = nullptr) {
+    std::vector<int32_t> T, pt;
+    if (!fetch(T, c.seq_lens, c.B, stream)) return BSA_ERR_HIP;
+    const int64_t cap = static_cast<int64_t>(c.max_blocks) * c.block;
+    for (int s = 0; s < c.B; ++s)
+        if (T[s] < lo || T[s] > cap) return BSA_ERR_CONTRACT;
+    if (!fetch(pt, c.page_table, static_cast<size_t>(c.B) * c.max_blocks, stream))
+        return BSA_ERR_HIP;
+    for (int s = 0; s < c.B; ++s)
+        for (int j = 0; j < blocks_of(T[s], c.block); ++j)
+            if (pt[static_cast<size_t>(s) * c.max_blocks + j] < 0) return BSA_ERR_CONTRACT;
+    if (T_out) *T_out = T;
+    return BSA_OK;
+}
+#else
+bsa_status contract_cache(const CacheArgs&, int64_t, hipStream_t) { return BSA_OK; }
+#endif
+
+// The kept lists of a decode: 0 <= cnt <= n_max, and the first cnt entries
+// of each idx row are distinct block ids below ceil(seq_lens / block), with
+// finite biases when a bias is given.
+#if BSA_CHECKED
+bsa_status contract_kept(const CacheArgs& c, const int32_t* idx, const int32_t* cnt,
+                         const float* bias, int n_max, hipStream_t stream) {
+    std::vector<int32_t> T, ci, ix;
+    std::vector<float> bs;
+    bsa_status st = contract_cache(c, 0, stream, &T);
+    if (st != BSA_OK) return st;
+    const size_t groups = static_cast<size_t>(c.B) * c.Hkv;
+    if (!fetch(ci, cnt, groups, stream) || !fetch(ix, idx, groups * n_max, stream))
+        return BSA_ERR_HIP;
+    if (bias && !fetch(bs, bias, groups * n_max, stream)) return BSA_ERR_HIP;
+    for (size_t g = 0; g < groups; ++g) {
+        const int nb = blocks_of(T[g / c.Hkv], c.block);
+        if (ci[g] < 0 || ci[g] > n_max) return BSA_ERR_CONTRACT;
+        std::vector<char> seen(nb, 0);
+        for (int k = 0; k < ci[g]; ++k) {
+            const int32_t j = ix[g * n_max + k];
+            if (j < 0 || j >= nb || seen[j]) return BSA_ERR_CONTRACT;
+            seen[j] = 1;
+            if (bias && !isfinite(bs[g * n_max + k])) return BSA_ERR_CONTRACT;
+        }
+    }
+    return BSA_OK;
+}
+#else
+bsa_status contract_kept(const CacheArgs&, const int32_t*, const int32_t*, const float*, int,
+                         hipStream_t) {
+    return BSA_OK;
+}
+#endif
+
 bsa_status sparse_decode(const bsa_layout* layout, const bsa_cache* cache, const void* q,
                          const int32_t* idx, const int32_t* cnt, const float* bias, int32_t n_max,
                          float softmax_scale, void* o, float* lse, void* ws, size_t ws_bytes,
@@ -120,6 +210,7 @@ bsa_status sparse_decode(const bsa_layout* layout, const bsa_cache* cache, const
     const CacheArgs c = make_args(layout, cache);
     const DecodeWs w = decode_ws(c, n_max);
     if (ws_bytes < w.total) return BSA_ERR_WORKSPACE;
+    if ((st = contract_kept(c, idx, cnt, bias, n_max, stream)) != BSA_OK) return st;
     DecodeArgs a;
     a.q = q;
     a.idx = idx;
@@ -148,6 +239,7 @@ const char* bsa_status_string(bsa_status status) {
         case BSA_ERR_PARAM: return "parameter out of range";
         case BSA_ERR_WORKSPACE: return "workspace too small";
         case BSA_ERR_HIP: return "HIP kernel launch failed";
+        case BSA_ERR_CONTRACT: return "a device-side input breaks its contract (checked build)";
     }
     return "unknown status";
 }
@@ -187,6 +279,7 @@ bsa_status bsa_build_block_desc(const bsa_layout* layout, const bsa_cache* cache
         if (range_begin) return BSA_ERR_PARAM;
     }
     const CacheArgs c = make_args(layout, cache);
+    if ((st = contract_cache(c, append ? n_new : 0, stream)) != BSA_OK) return st;
     return hip_status(launch_kv_write(c, append ? kModeAppend : kModeRebuild, k_new, v_new,
                                       append ? n_new : 0, range_begin, stream));
 }
@@ -202,6 +295,7 @@ bsa_status bsa_select_blocks(const bsa_layout* layout, const bsa_cache* cache, c
     const CacheArgs c = make_args(layout, cache);
     if (topn_keys_per_thread(c.max_blocks) == 0) return BSA_ERR_UNSUPPORTED;
     if (ws_bytes < select_ws(c)) return BSA_ERR_WORKSPACE;
+    if ((st = contract_cache(c, 0, stream)) != BSA_OK) return st;
     SelectArgs s;
     s.q = q;
     s.gate_w = params->gate_w;
@@ -230,6 +324,7 @@ bsa_status bsa_append_select(const bsa_layout* layout, const bsa_cache* cache, c
     const CacheArgs c = make_args(layout, cache);
     if (topn_keys_per_thread(c.max_blocks) == 0) return BSA_ERR_UNSUPPORTED;
     if (ws_bytes < select_ws(c)) return BSA_ERR_WORKSPACE;
+    if ((st = contract_cache(c, 1, stream)) != BSA_OK) return st;
     SelectArgs s;
     s.q = q;
     s.gate_w = params->gate_w;
@@ -279,6 +374,7 @@ bsa_status bsa_rectify_chunk(const bsa_layout* layout, const bsa_cache* cache, c
     const CacheArgs c = make_args(layout, cache);
     const RectifyWs w = rectify_ws(c, f);
     if (ws_bytes < w.total) return BSA_ERR_WORKSPACE;
+    if ((st = contract_cache(c, f, stream)) != BSA_OK) return st;
     RectifyArgs a;
     a.q = q;
     a.k_new = k_new;

@@ -40,6 +40,20 @@
  *   (hipGetLastError after the launches).  Device-side contracts (listed per
  *   call, e.g. seq_lens[b] <= max_blocks*block, page ids < num_pages) are not
  *   checked on the device; breaking them is undefined behaviour.
+ * Checked build.  libbsa_checked.so exports the same entry points, built with
+ *   BSA_CHECKED=1.  Each call first drains `stream`, copies the device values
+ *   its contracts bound to the host and returns BSA_ERR_CONTRACT, enqueuing
+ *   nothing, if one of these is broken:
+ *     every call:   0 <= seq_lens[s] <= max_blocks*block, and every block
+ *                   holding tokens has a page id >= 0 (the pool size is the
+ *                   caller's, so the upper bound is not checked);
+ *     append:       seq_lens[s] >= n_new (bsa_append_select: >= 1);
+ *     decode:       0 <= cnt <= n_max, the first cnt ids of each idx row are
+ *                   distinct and below ceil(seq_lens[s] / block), and their
+ *                   gate biases (gated call) are finite;
+ *     rectify:      seq_lens[s] >= f.
+ *   A failed copy returns BSA_ERR_HIP.  The checked build synchronises on
+ *   every call: it is for debugging and cannot be captured into a graph.
  * Numbers.  q and o use the KV dtype; lse is fp32, the natural log of the sum
  *   over attended tokens of exp(softmax_scale * q.k); accumulation is fp32.
  *
@@ -92,7 +106,9 @@ typedef enum bsa_status {
     BSA_ERR_UNSUPPORTED = 3, /* dtype, d, block or descriptor kind not built */
     BSA_ERR_PARAM = 4,       /* selection / rectify parameter out of range */
     BSA_ERR_WORKSPACE = 5,   /* ws too small (see bsa_workspace_size) */
-    BSA_ERR_HIP = 6          /* a kernel launch failed */
+    BSA_ERR_HIP = 6,         /* a kernel launch failed */
+    BSA_ERR_CONTRACT = 7     /* checked build only: a device-side input breaks
+                                its contract (see "Checked build" above) */
 } bsa_status;
 
 typedef enum bsa_dtype { BSA_DTYPE_F32 = 0, BSA_DTYPE_BF16 = 1 } bsa_dtype;

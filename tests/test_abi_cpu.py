@@ -45,9 +45,44 @@ def test_no_internal_symbols_exported():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert bsa.status_string(s)
+    assert "contract" in bsa.status_string(bsa.ERR_CONTRACT)
     assert bsa.status_string(99) == "unknown status"
+
+
+@pytest.fixture
+def checked_lib():
+    before = bsa.use_library(bsa.LIB_CHECKED)
+    try:
+        yield bsa.lib()
+    finally:
+        bsa.use_library(before)
+
+
+def test_checked_library_exports_the_same_symbols(checked_lib):
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", bsa.LIB_CHECKED], capture_output=True,
+                         text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert {s for s in syms if s.startswith("bsa_")} == set(declared_functions())
+    for n in declared_functions():
+        assert hasattr(checked_lib, n), n
+
+
+def test_checked_library_validates_host_arguments_first(checked_lib):
+    # host-side validation still runs before any HIP call, so these statuses
+    # come back without a device (the contract checks would need one)
+    fake = ctypes.c_void_p(0x1000)
+    C = bsa.c_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    for kw, status in [(dict(Hq=30), bsa.ERR_SHAPE), (dict(d=96), bsa.ERR_UNSUPPORTED)]:
+        st = checked_lib.bsa_build_block_desc(ctypes.byref(L_ok(**kw).c()), ctypes.byref(C),
+                                              fake, fake, 1, None, None)
+        assert st == status
+    P = bsa.SelectParams(sparsity_bp=9000, n_local=2, n_max=10)
+    assert _select(L_ok(), P, q=0) == bsa.ERR_NULL
+    assert _select(L_ok(), P, ws_bytes=16) == bsa.ERR_WORKSPACE
+    assert _select(L_ok(), bsa.SelectParams(sparsity_bp=9000, n_local=0, n_max=10)) == bsa.ERR_PARAM
 
 
 def L_ok(**kw):
