@@ -56,6 +56,10 @@ constexpr int kScoreIters = BSA_SCORE_ITERS;
 constexpr int kTopnThreads = 1024;
 constexpr int kTopnWaves = kTopnThreads / kWave;
 constexpr int kAliveCap = 2048;  // keys gathered after the first radix pass
+// word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data
+// format, no swizzle): stores through it are range-checked against the
+// descriptor's byte count
+constexpr int kBufferWord3 = 0x00020000;
 
 struct ScoreParams {
     CacheArgs c;
@@ -276,6 +280,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     __shared__ uint32_t res_s[2];
     __shared__ uint32_t red_min[kTopnWaves], red_max[kTopnWaves];
     __shared__ float red_z[kTopnWaves];
+    __shared__ uint32_t w0keys[KPT * kWave];  // wave 0's keys, slot r * 64 + lane
 
     const int grp = blockIdx.x;
     const int s = grp / c.Hkv;
@@ -322,52 +327,83 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         }
     }
 
+    // mode: 0 = pick none, 1 = pick every candidate, 2 = threshold select
+    const int mode = (K <= 0) ? 0 : (K >= NC ? 1 : 2);
+
     // Log-gate bias ("Simple Attention Sparsification", Method): gates are
     // softmax(tau * s) over all NC candidates, so a kept candidate's bias is
-    // tau * (s_j - smax) - ln sum_c exp(tau * (s_c - smax)).  The red_max
-    // slots are read before the second barrier and rewritten only after it.
+    // tau * (s_j - smax) - ln sum_c exp(tau * (s_c - smax)).  smax is the
+    // largest key, which the threshold select reduces anyway; each wave's
+    // part of the sum goes to red_z and is added up after a barrier the
+    // select already has.  In the threshold select the parts are formed
+    // while wave 0 alone finishes the radix passes and the other waves
+    // would only wait: wave 1 also forms wave 0's part, from a copy of
+    // wave 0's keys in LDS.
+    // Only picked candidates carry a bias, so with nothing picked there is
+    // no normaliser to form.
     float* bias_out = a.gate_bias ? a.gate_bias + static_cast<int64_t>(grp) * a.n_max : nullptr;
+    const bool gated = bias_out != nullptr && mode != 0;  // uniform
+    const float tau_l2 = a.gate_tau * kLog2e;
     float g_smax = 0.f, g_lnz = 0.f;
-    if (bias_out && NC > 0) {
-        uint32_t lmax = 0u;
-        if (live) {
-#pragma unroll
-            for (int r = 0; r < KPT; ++r)
-                if (base + r < NC) lmax = max(lmax, key[r]);
-        }
-        lmax = wave_max_u32(lmax);
-        if (lane == 0) red_max[wave] = lmax;
-        __syncthreads();
-        uint32_t kmx = 0u;
-#pragma unroll
-        for (int w = 0; w < kTopnWaves; ++w) kmx = max(kmx, red_max[w]);
-        g_smax = key_float(kmx);
+    // this wave's part of sum_c exp(tau * (s_c - smax)), into red_z[wave]
+    auto gate_sum_part = [&]() __attribute__((always_inline)) {
         float z = 0.f;
         if (live) {
 #pragma unroll
             for (int r = 0; r < KPT; ++r)
-                if (base + r < NC) z += expf(a.gate_tau * (key_float(key[r]) - g_smax));
+                if (key[r] != 0u)
+                    z += __builtin_amdgcn_exp2f(tau_l2 * (key_float(key[r]) - g_smax));
         }
         z = wave_sum(z);
         if (lane == 0) red_z[wave] = z;
-        __syncthreads();
+    };
+    // wave 0's part, formed by another wave from w0keys (the same terms in
+    // the same order as wave 0 would add them)
+    auto gate_sum_wave0 = [&]() __attribute__((always_inline)) {
+        float z = 0.f;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            const uint32_t k = w0keys[r * kWave + lane];
+            if (k != 0u) z += __builtin_amdgcn_exp2f(tau_l2 * (key_float(k) - g_smax));
+        }
+        z = wave_sum(z);
+        if (lane == 0) red_z[0] = z;
+    };
+    auto gate_finish = [&]() __attribute__((always_inline)) {  // after a barrier
         float zt = 0.f;
 #pragma unroll
         for (int w = 0; w < kTopnWaves; ++w) zt += red_z[w];
         g_lnz = logf(zt);
-    }
+    };
     auto gate = [&](uint32_t k) __attribute__((always_inline)) {
         return a.gate_tau * (key_float(k) - g_smax) - g_lnz;
     };
 
-    // mode: 0 = pick none, 1 = pick every candidate, 2 = threshold select
-    const int mode = (K <= 0) ? 0 : (K >= NC ? 1 : 2);
-    if (mode == 1 && live) {
+    if (mode == 1) {
+        if (gated) {
+            uint32_t lmax = 0u;
+            if (live) {
 #pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-            if (base + r < NC) {
-                out[base + r] = base + r;
-                if (bias_out) bias_out[base + r] = gate(key[r]);
+                for (int r = 0; r < KPT; ++r) lmax = max(lmax, key[r]);
+            }
+            lmax = wave_max_u32(lmax);
+            if (lane == 0) red_max[wave] = lmax;
+            __syncthreads();
+            uint32_t kmx = 0u;
+#pragma unroll
+            for (int w = 0; w < kTopnWaves; ++w) kmx = max(kmx, red_max[w]);
+            g_smax = key_float(kmx);
+            gate_sum_part();
+            __syncthreads();
+            gate_finish();
+        }
+        if (live) {
+#pragma unroll
+            for (int r = 0; r < KPT; ++r) {
+                if (base + r < NC) {
+                    out[base + r] = base + r;
+                    if (gated) bias_out[base + r] = gate(key[r]);
+                }
             }
         }
     }
@@ -397,6 +433,8 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             kmax = max(kmax, red_max[w]);
         }
         kmin += 1u;
+        g_smax = key_float(kmax);
+        bool z_pending = gated;  // the normaliser's parts are still to form
         const uint32_t range = kmax - kmin;
         uint32_t prefix = 0;  // of key - kmin, above the current digit
         int krem = K;
@@ -487,8 +525,13 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
                         if (am & (1u << r)) alive_s[at++] = key[r] - kmin;
                     }
                 }
+                if (z_pending && wave == 0) {
+#pragma unroll
+                    for (int r = 0; r < KPT; ++r) w0keys[r * kWave + lane] = key[r];
+                }
                 __syncthreads();
                 if (wave == 0) {
+                    __builtin_amdgcn_s_setprio(2);  // the other waves only wait for it
                     while (shift > 0) {
                         const int dbits = min(8, shift);
                         shift -= dbits;
@@ -510,7 +553,12 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
                         res_s[0] = prefix;
                         res_s[1] = static_cast<uint32_t>(krem);
                     }
+                    __builtin_amdgcn_s_setprio(0);
+                } else if (z_pending) {
+                    gate_sum_part();
+                    if (wave == 1) gate_sum_wave0();
                 }
+                z_pending = false;
                 __syncthreads();
                 prefix = res_s[0];
                 krem = static_cast<int>(res_s[1]);
@@ -520,6 +568,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         }
         tau = kmin + prefix;
         need_eq = krem;
+        if (z_pending) gate_sum_part();  // added up after the scan's barrier below
 
         // one packed scan: (keys > tau) << 16 | (keys == tau), per thread;
         // the positions of those keys are kept as bit masks
@@ -536,6 +585,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         const int incl = wave_incl_scan(packed);
         if (lane == 63) wsum[wave] = incl;
         __syncthreads();
+        if (gated) gate_finish();
         int before = 0;
 #pragma unroll
         for (int w = 0; w < kTopnWaves; ++w) before += (w < wave) ? wsum[w] : 0;
@@ -549,22 +599,40 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             take_m |= eq_m & (0u - eq_m);
             eq_m &= eq_m - 1u;
         }
-        if (bias_out && live) {
+        // only the taken keys, lowest index first.  The rows are written
+        // through buffer descriptors sized to n_max entries: a store takes a
+        // 32-bit byte offset, and the hardware drops a store past the row
+        // (pos >= n_max), which replaces the bounds test.
+        const __amdgpu_buffer_rsrc_t out_rs = __builtin_amdgcn_make_buffer_rsrc(
+            out, 0, a.n_max * static_cast<int>(sizeof(int32_t)), kBufferWord3);
+        int off = pos * static_cast<int>(sizeof(int32_t));
+        if (gated) {
+            const __amdgpu_buffer_rsrc_t bias_rs = __builtin_amdgcn_make_buffer_rsrc(
+                bias_out, 0, a.n_max * static_cast<int>(sizeof(float)), kBufferWord3);
+            // a taken key's bias needs the key itself: the keys are walked in
+            // groups of four, so picking one out of the registers takes a
+            // three-step select chain (no dynamic register indexing)
+            constexpr int GS = KPT < 4 ? KPT : 4;
 #pragma unroll
-            for (int r = 0; r < KPT; ++r) {
-                if ((take_m >> r) & 1u) {
-                    if (pos < a.n_max) {
-                        out[pos] = base + r;
-                        bias_out[pos] = gate(key[r]);
-                    }
-                    ++pos;
+            for (int g0 = 0; g0 < KPT; g0 += GS) {
+                uint32_t m = (take_m >> g0) & ((1u << GS) - 1u);
+                while (m != 0u) {
+                    const int rr = __builtin_ctz(m);
+                    uint32_t kk = key[g0];
+#pragma unroll
+                    for (int i = 1; i < GS; ++i) kk = (rr == i) ? key[g0 + i] : kk;
+                    __builtin_amdgcn_raw_buffer_store_b32(base + g0 + rr, out_rs, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(gate(kk)), bias_rs, off,
+                                                          0, 0);
+                    off += static_cast<int>(sizeof(int32_t));
+                    m &= m - 1u;
                 }
             }
         } else {
-            // only the taken keys, lowest index first
             while (take_m != 0u) {
-                if (pos < a.n_max) out[pos] = base + __builtin_ctz(take_m);
-                ++pos;
+                __builtin_amdgcn_raw_buffer_store_b32(base + __builtin_ctz(take_m), out_rs, off, 0,
+                                                      0);
+                off += static_cast<int>(sizeof(int32_t));
                 take_m &= take_m - 1u;
             }
         }
