@@ -52,6 +52,12 @@ namespace {
 #ifndef BSA_DECODE_UNIT_LDS
 #define BSA_DECODE_UNIT_LDS (112 * 1024)  // LDS bytes for the per-unit partials
 #endif
+#ifndef BSA_DECODE_UNITS_PER_SPLIT
+#define BSA_DECODE_UNITS_PER_SPLIT 8  // units a split is cut into: one per wave
+#endif
+#ifndef BSA_DECODE_MAX_UNIT
+#define BSA_DECODE_MAX_UNIT 8  // most tiles per unit, unless the LDS slots need more
+#endif
 constexpr int kLdsBytes = 160 * 1024;      // LDS of one CU
 constexpr int kMaxSplitBlocks = 4096;      // kept blocks one split may cover
 constexpr int kThreads = 256;     // fp32 kernel
@@ -584,8 +590,10 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 template <int D, int BLK>
 hipError_t launch_bf16(DecodeParams p, hipStream_t stream) {
     const bool gate = p.a.bias != nullptr;
-    // units: as many LDS partial slots as the budget holds, each unit at
-    // least two tiles; the split's tiles / units tiles per unit
+    // units: about one per wave, of 2 to BSA_DECODE_MAX_UNIT tiles (fewer,
+    // longer units mean fewer partials to flush and merge, and waves that
+    // the hardware serves faster still take the spare units); longer units
+    // only when the split has more units than the LDS holds partial slots
     const int tiles = (p.a.n_max * (BLK / 32) + p.a.splits - 1) / p.a.splits;
     const int unit_bytes = static_cast<int>(sizeof(float)) * (32 + p.c.G * D);
     // the split's block ids, page ids (and biases) take what they need; the
@@ -593,8 +601,9 @@ hipError_t launch_bf16(DecodeParams p, hipStream_t stream) {
     const int id_bytes = (gate ? 3 : 2) * static_cast<int>(sizeof(int)) * p.max_blocks_per_wg;
     const int budget = min(BSA_DECODE_UNIT_LDS, kLdsBytes - 256 - id_bytes);
     const int slots = budget / unit_bytes;
-    int ut = (tiles + slots - 1) / slots;
-    if (ut < 2) ut = 2;
+    int ut = (tiles + BSA_DECODE_UNITS_PER_SPLIT - 1) / BSA_DECODE_UNITS_PER_SPLIT;
+    ut = min(max(ut, 2), BSA_DECODE_MAX_UNIT);
+    ut = max(ut, (tiles + slots - 1) / slots);
     p.unit_tiles = ut;
     p.max_units = (tiles + ut - 1) / ut;
     const size_t shm = static_cast<size_t>(unit_bytes) * p.max_units + id_bytes;
