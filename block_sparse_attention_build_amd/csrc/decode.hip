@@ -109,12 +109,11 @@ __device__ __forceinline__ void merge_waves_and_store(const float* sm, const flo
 
 // The bf16 kernel: one workgroup of kDecThreads (8 waves) per (sequence, KV
 // head, split), one workgroup per CU.  The split's kept tiles are cut into
-// units of unit_tiles tiles; waves claim units one at a time from an LDS
-// counter, so a wave that the hardware serves faster simply takes more units
-// and all waves finish together.  Each unit leaves its own partial
-// (running max, sum, unnormalised O) in LDS, and the units are merged in
-// unit order at the end, so the result does not depend on which wave took
-// which unit.
+// units of unit_tiles tiles (about one per wave); waves claim units one at a
+// time from an LDS counter, so a wave that the hardware serves faster takes
+// any spare unit.  Each unit leaves its own partial (running max, sum,
+// unnormalised O) in LDS, and the units are merged in unit order at the
+// end, so the result does not depend on which wave took which unit.
 template <int D, int BLK, bool GATE>
 __global__ __launch_bounds__(kDecThreads)
 __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf16_kernel(
