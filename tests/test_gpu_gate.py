@@ -207,3 +207,58 @@ def test_gated_decode_constant_bias_is_shifted_plain_decode():
         outs.append((o.float().cpu(), lse.cpu()))
     assert (outs[0][0] - outs[1][0]).abs().max().item() <= 1e-2
     assert ((outs[1][1] - (outs[0][1] - 1.5)).abs() / outs[0][1].abs().clamp(min=1)).max() <= 1e-5
+
+
+def test_gated_topn_long_row_of_ties():
+    """The gated selection on about 8000 almost-tied candidates: the
+    threshold digit holds more keys than the gathered list takes, so the
+    whole-workgroup radix passes run and the normaliser's parts are formed
+    after them rather than beside the wave-0 passes.  Selection, biases and
+    the gated decode against the oracle."""
+    import torch
+    import workloads as W
+    d, blk, Hq, Hkv = 64, 32, 4, 1
+    T = 8000 * blk + 17
+    L = bsa.Layout(1, Hq, Hkv, d, blk, (T + blk - 1) // blk + 1, BF16, MINMAX)
+    P = bsa.SelectParams(budget_tokens=0, sparsity_bp=9000, n_local=1, n_min=0)
+    P.n_max = bsa.block_count(P, L.max_blocks, blk)
+    rng = np.random.Generator(np.random.PCG64(124))
+    q = W.quantize(rng.standard_normal((1, Hq, d), dtype=np.float32), "bf16")
+    u = W.group_direction(q[0])
+    tmpl = rng.standard_normal((blk, d), dtype=np.float32)
+    K = np.tile(tmpl, ((T + blk - 1) // blk, 1))[:T].copy()
+    K[-17:] = rng.standard_normal((17, d), dtype=np.float32)
+    for j in (7, 1000, 4321, 7777, 7990):   # clearly above the tied mass
+        K[j * blk:(j + 1) * blk] += 3.0 * u
+    for j in (3, 2500, 6000):               # clearly below it
+        K[j * blk:(j + 1) * blk] -= 3.0 * u
+    Ks = [W.quantize(K, "bf16")[None]]
+    Vs = [W.quantize(rng.standard_normal((1, T, d), dtype=np.float32), "bf16")]
+    tau = 0.05
+    cache = bsa.allocate_cache(L, page_table=random_page_table(L, 10))
+    prefill(L, cache, Ks, Vs, [T])
+    dev = "cuda"
+    idx = torch.full((1, Hkv, P.n_max), -7, dtype=torch.int32, device=dev)
+    cnt = torch.full((1, Hkv), -7, dtype=torch.int32, device=dev)
+    P.gate_tau = tau
+    P.gate_bias = torch.full((1, Hkv, P.n_max), float("nan"), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(bsa.workspace_size(L, bsa.OP_SELECT, P.n_max),
+                         bsa.workspace_size(L, bsa.OP_DECODE, P.n_max)),
+                     dtype=torch.uint8, device=dev)
+    q_dev = to_dev(q, L)
+    bsa.select_blocks(L, cache, q_dev, P, idx, cnt, ws)
+    o = torch.full((1, Hq, d), float("nan"), dtype=q_dev.dtype, device=dev)
+    lse = torch.full((1, Hq), float("nan"), dtype=torch.float32, device=dev)
+    bsa.sparse_decode_gated(L, cache, q_dev, idx, cnt, P.gate_bias, P.n_max, 1.0 / math.sqrt(d),
+                            o, lse, ws)
+    torch.cuda.synchronize()
+    ref, rbias, smax = _oracle_gated(L, P, q, Ks, Vs, [T], tau, None)
+    compare_step(L, idx, cnt, o, lse, ref)
+    assert {7, 1000, 4321, 7777, 7990} <= set(ref[(0, 0)][0].tolist())
+    c = int(cnt[0, 0])
+    NC = -(-T // blk) - 1
+    tol = tau * 2e-5 * smax + 1e-4 + NC * 1.2e-7
+    gb = P.gate_bias.cpu().numpy()
+    err = np.abs(gb[0, 0, :c] - rbias[(0, 0)]).max()
+    assert err <= tol, (err, tol)
+    assert np.all(gb[0, 0, c:] == 0.0)
