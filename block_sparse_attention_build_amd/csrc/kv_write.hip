@@ -18,10 +18,15 @@ namespace bsa {
 namespace {
 
 constexpr int kThreads = 128;
+// loads in flight per thread: a rectify overwrite or a rebuild walks whole
+// blocks with few workgroups, so its time is the number of dependent
+// round trips (a 64-token block in two instead of eight)
+constexpr int kBatch = 32;
 
 template <int DT, int DESC>
 __global__ __launch_bounds__(kThreads) void kv_write_kernel(KvWriteParams p) {
-    kv_write_block<DT, DESC, kThreads>(p, static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y));
+    kv_write_block<DT, DESC, kThreads, kBatch>(p, static_cast<int>(blockIdx.x),
+                                               static_cast<int>(blockIdx.y));
 }
 
 template <int DT, int DESC>

@@ -10,7 +10,7 @@
 // tokens in order to update or rebuild that channel's descriptor.  New-token
 // values are read from the source, older ones from the cache, so there is no
 // read-after-write hazard inside the workgroup.  Work per step is a few KiB,
-// so the body is latency-bound: every thread keeps kKvBatch loads in flight.
+// so the body is latency-bound: every thread keeps KB loads in flight.
 #pragma once
 
 #include "bsa_device.h"
@@ -18,7 +18,7 @@
 
 namespace bsa {
 
-constexpr int kKvBatch = 8;  // loads in flight per thread
+constexpr int kKvBatch = 8;  // loads in flight per thread (default)
 
 struct KvWriteParams {
     CacheArgs c;
@@ -30,8 +30,9 @@ struct KvWriteParams {
 };
 
 // One (sequence, KV head, block) of the write: bx = block offset from the
-// first touched block, grp = sequence * Hkv + KV head; NT threads.
-template <int DT, int DESC, int NT>
+// first touched block, grp = sequence * Hkv + KV head; NT threads, KB loads
+// in flight per thread.
+template <int DT, int DESC, int NT, int KB = kKvBatch>
 __device__ __forceinline__ void kv_write_block(const KvWriteParams& p, int bx, int grp) {
     typedef typename Elem<DT>::T E;
     const CacheArgs& c = p.c;
@@ -62,17 +63,17 @@ __device__ __forceinline__ void kv_write_block(const KvWriteParams& p, int bx, i
                          : nullptr;
 
     if (writes) {
-        // copy: kKvBatch independent source loads per thread before the stores
+        // copy: KB independent source loads per thread before the stores
         // (the stores could alias the sources as far as the compiler knows,
         // so without the batching every load would wait for the last store)
         const int w0 = max(tb0, lo);
         const int nel = (tb1 - w0) * d;
         const E* ksrc = ks + static_cast<int64_t>(w0 - lo) * d;
         const E* vsrc = vs + static_cast<int64_t>(w0 - lo) * d;
-        for (int e0 = threadIdx.x; e0 < nel; e0 += kKvBatch * NT) {
-            E kb[kKvBatch], vb[kKvBatch];
+        for (int e0 = threadIdx.x; e0 < nel; e0 += KB * NT) {
+            E kb[KB], vb[KB];
 #pragma unroll
-            for (int u = 0; u < kKvBatch; ++u) {
+            for (int u = 0; u < KB; ++u) {
                 const int e = e0 + u * NT;
                 if (e < nel) {
                     kb[u] = ksrc[e];
@@ -80,7 +81,7 @@ __device__ __forceinline__ void kv_write_block(const KvWriteParams& p, int bx, i
                 }
             }
 #pragma unroll
-            for (int u = 0; u < kKvBatch; ++u) {
+            for (int u = 0; u < KB; ++u) {
                 const int e = e0 + u * NT;
                 if (e < nel) {
                     const int tt = e / d;
@@ -94,7 +95,7 @@ __device__ __forceinline__ void kv_write_block(const KvWriteParams& p, int bx, i
     }
 
     // descriptor of block j, one thread per channel; the block's keys are
-    // read kKvBatch tokens at a time (independent loads), then folded in token
+    // read KB tokens at a time (independent loads), then folded in token
     // order
     const bool merge = (p.mode == kModeAppend) && (tb0 < lo);
     const int t_first = merge ? lo : tb0;
@@ -111,10 +112,10 @@ __device__ __forceinline__ void kv_write_block(const KvWriteParams& p, int bx, i
                 acc = static_cast<const float*>(c.desc)[drow * d + i];
             }
         }
-        for (int t0 = t_first; t0 < tb1; t0 += kKvBatch) {
-            float v[kKvBatch];
+        for (int t0 = t_first; t0 < tb1; t0 += KB) {
+            float v[KB];
 #pragma unroll
-            for (int u = 0; u < kKvBatch; ++u) {
+            for (int u = 0; u < KB; ++u) {
                 const int t = t0 + u;
                 v[u] = 0.f;
                 if (t < tb1)
@@ -122,7 +123,7 @@ __device__ __forceinline__ void kv_write_block(const KvWriteParams& p, int bx, i
                                                : Elem<DT>::load(kp, k_off<DT>(t - tb0, i, d));
             }
 #pragma unroll
-            for (int u = 0; u < kKvBatch; ++u) {
+            for (int u = 0; u < KB; ++u) {
                 if (t0 + u >= tb1) break;
                 if (DESC == kMinMax) {
                     mn = (!have || v[u] < mn) ? v[u] : mn;
