@@ -2,10 +2,11 @@
 
 A thin ctypes layer over the C ABI in include/bsa.h: the functions below have
 the C entry points' names and arguments, take torch tensors that live on the
-GPU, and pass their data pointers and the current HIP stream.  torch supplies
-device memory and streams only; every step of the computation runs in the
-library's HIP kernels.  There is no CPU fallback: if libbsa.so is missing or
-fails to load, every call raises.
+GPU, check that each is a contiguous GPU tensor of the documented dtype and
+at least the documented size, and pass their data pointers and the current
+HIP stream.  torch supplies device memory and streams only; every step of
+the computation runs in the library's HIP kernels.  There is no CPU
+fallback: if libbsa.so is missing or fails to load, every call raises.
 """
 import ctypes
 import os
@@ -117,6 +118,60 @@ def _check(status, what):
         raise BsaError(status, what)
 
 
+def _need(t, name, dtype, numel):
+    """t must be a contiguous GPU tensor of `dtype` (None: any) with at least
+    `numel` elements: the library reaches it through its data pointer alone,
+    so a wrong tensor is refused here rather than read out of bounds."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor, got one on {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: {t.numel()} elements, needs at least {numel}")
+
+
+def _need_cache(L, cache):
+    import torch
+    kv = L.torch_dtype()
+    _need(cache.k_pool, "k_pool", kv, L.Hkv * L.block * L.d)
+    _need(cache.v_pool, "v_pool", kv, L.Hkv * L.block * L.d)
+    _need(cache.page_table, "page_table", torch.int32, L.B * L.max_blocks)
+    _need(cache.seq_lens, "seq_lens", torch.int32, L.B)
+    if L.desc_kind == DESC_MINMAX:
+        _need(cache.desc, "desc", kv, L.B * L.Hkv * L.max_blocks * 2 * L.d)
+    else:
+        _need(cache.desc, "desc", torch.float32, L.B * L.Hkv * L.max_blocks * L.d)
+
+
+def _need_select(L, cache, q, params, idx, cnt, ws):
+    import torch
+    _need_cache(L, cache)
+    _need(q, "q", L.torch_dtype(), L.B * L.Hq * L.d)
+    _need(idx, "idx", torch.int32, L.B * L.Hkv * params.n_max)
+    _need(cnt, "cnt", torch.int32, L.B * L.Hkv)
+    _need(ws, "ws", None, 0)
+    if params.gate_w is not None:
+        _need(params.gate_w, "gate_w", torch.bfloat16, L.d * L.d)
+    if params.gate_bias is not None:
+        _need(params.gate_bias, "gate_bias", torch.float32, L.B * L.Hkv * params.n_max)
+
+
+def _need_decode(L, cache, q, idx, cnt, n_max, o, lse, ws):
+    import torch
+    _need_cache(L, cache)
+    _need(q, "q", L.torch_dtype(), L.B * L.Hq * L.d)
+    _need(idx, "idx", torch.int32, L.B * L.Hkv * n_max)
+    _need(cnt, "cnt", torch.int32, L.B * L.Hkv)
+    _need(o, "o", L.torch_dtype(), L.B * L.Hq * L.d)
+    _need(lse, "lse", torch.float32, L.B * L.Hq)
+    _need(ws, "ws", None, 0)
+
+
 # ---------------------------------------------------------------------------
 # Shape / parameter records
 # ---------------------------------------------------------------------------
@@ -220,6 +275,13 @@ def build_block_desc(layout: Layout, cache: Cache, k_new=None, v_new=None, n_new
                      range_begin=None, stream=None):
     """Append n_new tokens per sequence (k_new/v_new [B, Hkv, n_new, d]) or,
     with k_new = v_new = None, rebuild descriptors from range_begin [B]."""
+    import torch
+    _need_cache(layout, cache)
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        if t is not None:
+            _need(t, name, layout.torch_dtype(), layout.B * layout.Hkv * int(n_new) * layout.d)
+    if range_begin is not None:
+        _need(range_begin, "range_begin", torch.int32, layout.B)
     st = lib().bsa_build_block_desc(ctypes.byref(layout.c()), ctypes.byref(cache.c()),
                                     _ptr(k_new), _ptr(v_new), int(n_new), _ptr(range_begin),
                                     _stream(stream))
@@ -228,6 +290,7 @@ def build_block_desc(layout: Layout, cache: Cache, k_new=None, v_new=None, n_new
 
 def select_blocks(layout: Layout, cache: Cache, q, params: SelectParams, idx, cnt, ws,
                   stream=None):
+    _need_select(layout, cache, q, params, idx, cnt, ws)
     st = lib().bsa_select_blocks(ctypes.byref(layout.c()), ctypes.byref(cache.c()), _ptr(q),
                                  ctypes.byref(params.c()), _ptr(idx), _ptr(cnt), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream))
@@ -238,6 +301,9 @@ def append_select(layout: Layout, cache: Cache, k_new, v_new, q, params: SelectP
                   ws, stream=None):
     """build_block_desc (one token per sequence, k_new/v_new [B, Hkv, 1, d])
     followed by select_blocks, with the append sharing the scoring launch."""
+    _need_select(layout, cache, q, params, idx, cnt, ws)
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, name, layout.torch_dtype(), layout.B * layout.Hkv * layout.d)
     st = lib().bsa_append_select(ctypes.byref(layout.c()), ctypes.byref(cache.c()), _ptr(k_new),
                                  _ptr(v_new), _ptr(q), ctypes.byref(params.c()), _ptr(idx),
                                  _ptr(cnt), _ptr(ws), ws.numel() * ws.element_size(),
@@ -247,6 +313,7 @@ def append_select(layout: Layout, cache: Cache, k_new, v_new, q, params: SelectP
 
 def sparse_decode(layout: Layout, cache: Cache, q, idx, cnt, n_max: int, softmax_scale: float,
                   o, lse, ws, stream=None):
+    _need_decode(layout, cache, q, idx, cnt, n_max, o, lse, ws)
     st = lib().bsa_sparse_decode(ctypes.byref(layout.c()), ctypes.byref(cache.c()), _ptr(q),
                                  _ptr(idx), _ptr(cnt), int(n_max), float(softmax_scale), _ptr(o),
                                  _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
@@ -258,6 +325,9 @@ def sparse_decode_gated(layout: Layout, cache: Cache, q, idx, cnt, gate_bias, n_
                         softmax_scale: float, o, lse, ws, stream=None):
     """sparse_decode with gate_bias [B, Hkv, n_max] (fp32) added to the
     logits of every token of block idx[..., k]."""
+    import torch
+    _need_decode(layout, cache, q, idx, cnt, n_max, o, lse, ws)
+    _need(gate_bias, "gate_bias", torch.float32, layout.B * layout.Hkv * n_max)
     st = lib().bsa_sparse_decode_gated(ctypes.byref(layout.c()), ctypes.byref(cache.c()),
                                        _ptr(q), _ptr(idx), _ptr(cnt), _ptr(gate_bias), int(n_max),
                                        float(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws),
@@ -267,6 +337,15 @@ def sparse_decode_gated(layout: Layout, cache: Cache, q, idx, cnt, gate_bias, n_
 
 def rectify_chunk(layout: Layout, cache: Cache, q, k_new, v_new, f: int, softmax_scale: float,
                   o, lse, ws, stream=None):
+    import torch
+    L, kv = layout, layout.torch_dtype()
+    _need_cache(L, cache)
+    _need(q, "q", kv, L.B * L.Hq * int(f) * L.d)
+    _need(k_new, "k_new", kv, L.B * L.Hkv * int(f) * L.d)
+    _need(v_new, "v_new", kv, L.B * L.Hkv * int(f) * L.d)
+    _need(o, "o", kv, L.B * L.Hq * int(f) * L.d)
+    _need(lse, "lse", torch.float32, L.B * L.Hq * int(f))
+    _need(ws, "ws", None, 0)
     st = lib().bsa_rectify_chunk(ctypes.byref(layout.c()), ctypes.byref(cache.c()), _ptr(q),
                                  _ptr(k_new), _ptr(v_new), int(f), float(softmax_scale),
                                  _ptr(o), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),

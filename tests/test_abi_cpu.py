@@ -246,3 +246,31 @@ def test_host_block_count_matches_oracle():
         P = bsa.SelectParams(budget_tokens=budget, sparsity_bp=bp, n_local=nl, n_min=nm)
         for NB in [1, 2, 5, 33, 257, 513, 2049, 8193]:
             assert bsa.block_count(P, NB, 64) == O.block_count(NB, 64, budget, bp, nl, nm)
+
+
+def test_binding_refuses_host_tensors_and_non_tensors():
+    """The Python wrappers hand the library data pointers only, so they check
+    every tensor first: a host tensor or a non-tensor is refused before any
+    library call (the GPU-side dtype, layout and size checks are in
+    tests/test_gpu_binding.py)."""
+    import torch
+    L = bsa.Layout(1, 4, 1, 64, 64, 4, bsa.DTYPE_F32, bsa.DESC_MINMAX)
+    C = bsa.Cache(torch.zeros(4, 1, 64 * 64), torch.zeros(4, 1, 64 * 64),
+                  torch.zeros(1, 4, dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+                  torch.zeros(1, 1, 4, 2, 64))
+    q = torch.zeros(1, 4, 64)
+    idx = torch.zeros(1, 1, 2, dtype=torch.int32)
+    cnt = torch.zeros(1, 1, dtype=torch.int32)
+    o, lse, ws = torch.zeros(1, 4, 64), torch.zeros(1, 4), torch.zeros(1024, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        bsa.sparse_decode(L, C, q, idx, cnt, 2, 0.125, o, lse, ws)
+    P = bsa.SelectParams(budget_tokens=128, n_local=1, n_max=2)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        bsa.select_blocks(L, C, q, P, idx, cnt, ws)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        bsa.build_block_desc(L, C)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        bsa.rectify_chunk(L, C, q, q, q, 1, 0.125, o, lse, ws)
+    C_list = bsa.Cache([0.0], C.v_pool, C.page_table, C.seq_lens, C.desc)
+    with pytest.raises(TypeError, match="torch tensor"):
+        bsa.sparse_decode(L, C_list, q, idx, cnt, 2, 0.125, o, lse, ws)
