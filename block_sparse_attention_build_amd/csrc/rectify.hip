@@ -312,39 +312,42 @@ void rectify_bf16_kernel(RectifyParams p) {
             const int tok0 = 32 * t;
             const int nvalid = T - tok0;  // >= 1
             u32x4 vr[NT];
+            // S^T of every row tile first: the matrix cores work on the later
+            // row tiles' products while the softmax of the first one runs
+            floatx4 sacc_rt[RTW][2];
 #pragma unroll
-            for (int rt = 0; rt < RTW; ++rt) {
-                floatx4 sacc[2];
+            for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
                 for (int mt = 0; mt < 2; ++mt) {
-                    sacc[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    sacc_rt[rt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks)
-                        sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, kr[mt * KS + ks]), qb[rt][ks], sacc[mt], 0, 0, 0);
+                        sacc_rt[rt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, kr[mt * KS + ks]), qb[rt][ks], sacc_rt[rt][mt],
+                            0, 0, 0);
                 }
-                if (rt == 0) {
-                    // V operands are read once the K operands are consumed, which
-                    // keeps both out of registers at the same time
-                    asm volatile("" ::: "memory");
+            // V operands are read once the K operands are consumed, which
+            // keeps both out of registers at the same time
+            asm volatile("" ::: "memory");
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) vr[n] = *reinterpret_cast<const u32x4*>(vs_lds + n * 512);
-                    if (nvalid < 32) {  // zero V of the tokens past T (ragged last tile)
+            for (int n = 0; n < NT; ++n) vr[n] = *reinterpret_cast<const u32x4*>(vs_lds + n * 512);
+            if (nvalid < 32) {  // zero V of the tokens past T (ragged last tile)
 #pragma unroll
-                        for (int kk = 0; kk < 8; ++kk) {
-                            const int tok = (kk < 4) ? (4 * g + kk) : (16 + 4 * g + kk - 4);
-                            if (tok >= nvalid) {
-                                const uint32_t keep = (kk & 1) ? 0x0000ffffu : 0xffff0000u;
+                for (int kk = 0; kk < 8; ++kk) {
+                    const int tok = (kk < 4) ? (4 * g + kk) : (16 + 4 * g + kk - 4);
+                    if (tok >= nvalid) {
+                        const uint32_t keep = (kk & 1) ? 0x0000ffffu : 0xffff0000u;
 #pragma unroll
-                                for (int n = 0; n < NT; ++n) vr[n][kk >> 1] &= keep;
-                            }
-                        }
+                        for (int n = 0; n < NT; ++n) vr[n][kk >> 1] &= keep;
                     }
                 }
+            }
+#pragma unroll
+            for (int rt = 0; rt < RTW; ++rt) {
                 // raw scores; the scale is folded into the exponent below
                 float x[8];
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) x[kk] = sacc[kk >> 2][kk & 3];
+                for (int kk = 0; kk < 8; ++kk) x[kk] = sacc_rt[rt][kk >> 2][kk & 3];
                 if (tok0 + 31 > T - f) {  // the causal mask only bites in the last f tokens
 #pragma unroll
                     for (int kk = 0; kk < 8; ++kk) {
