@@ -16,10 +16,11 @@
 // shares to a fixed number of workgroups (two per CU), so ragged lengths
 // cost no load imbalance; each run of a share inside one group yields one
 // partial (o, base-2 lse) per row, merged afterwards in list order.
-// K/V tiles (16 KiB at d = 128) stream through a 4-stage LDS ring fed by
-// direct global->LDS copies, three tiles ahead of the one being computed;
-// every wave reads its matrix operands from LDS with conflict-free 16-byte
-// reads.  Per tile and 16-row tile: S^T = K Q^T (2 x d/32 MFMAs), causal
+// K/V tiles (16 KiB at d = 128) stream through an LDS ring fed by direct
+// global->LDS copies, two (4 stages, two workgroups per CU) or four (6
+// stages, one per CU) tiles ahead of the one being computed, with one
+// workgroup barrier per tile; every wave reads its matrix operands from LDS
+// with conflict-free 16-byte reads.  Per tile and 16-row tile: S^T = K Q^T (2 x d/32 MFMAs), causal
 // mask, online softmax with a lazily moved reference max, O += P V with P in
 // bf16 (d/16 MFMAs).
 //
@@ -50,6 +51,9 @@ constexpr int kWaves = kThreads / kWave;
 constexpr float kRebase = 8.f;  // log2 headroom before the running max is moved
 constexpr int kChunkTiles = BSA_RECTIFY_CHUNK_TILES;  // 32-token tiles per workgroup
 constexpr int kStages = BSA_RECTIFY_STAGES;           // tiles in flight per workgroup (LDS ring)
+#ifndef BSA_RECTIFY_STAGES_WIDE
+#define BSA_RECTIFY_STAGES_WIDE 6  // ring stages of the one-workgroup-per-CU shape
+#endif
 
 struct RectifyParams {
     CacheArgs c;
@@ -161,7 +165,7 @@ void rectify_bf16_kernel(RectifyParams p) {
     constexpr int RWG = 16 * RTW * NW;          // rows per workgroup (row group)
     static_assert(CPW >= 1 && CPW * NW == CH, "chunks split evenly over the waves");
     // NS-stage ring of tiles in LDS, filled by direct global->LDS copies
-    // (copy16_to_lds): each wave copies CPW KiB chunks per tile, NS-1 tiles
+    // (copy16_to_lds): each wave copies CPW KiB chunks per tile, NS-2 tiles
     // ahead of the one being computed, without using registers.
     __shared__ __attribute__((aligned(16))) uint16_t ring[NS][2 * TILE_EL];
     __shared__ int s_page[kMaxTilesPerWG * 32 / BLK + 2];
@@ -287,18 +291,21 @@ void rectify_bf16_kernel(RectifyParams p) {
             }
         };
 
+        // One barrier per tile.  Tiles are copied DIST = NS - 2 ahead, so the
+        // stage refilled in iteration k last held tile k - 2; every wave has
+        // finished computing tile k - 2 before it reached the barrier of
+        // iteration k - 1, which the refilling wave has passed.
+        constexpr int DIST = NS - 2;
+        static_assert(DIST >= 1, "ring stages");
 #pragma unroll
-        for (int k = 0; k < NS - 1; ++k)
+        for (int k = 0; k < DIST; ++k)
             if (k < nt) issue(t0 + k, k);
         for (int k = 0; k < nt; ++k) {
             const int t = t0 + k;
             const uint16_t* st = ring[k % NS];
-            // every wave is done reading the stage refilled next (it held tile k-1)
-            __builtin_amdgcn_s_barrier();
-            asm volatile("" ::: "memory");
-            if (k + NS - 1 < nt) {
-                issue(t + NS - 1, (k + NS - 1) % NS);
-                wait_vmcnt<CPW * (NS - 1)>();  // this wave's copies of tile k have landed
+            if (k + DIST < nt) {
+                issue(t + DIST, (k + DIST) % NS);
+                wait_vmcnt<CPW * DIST>();  // this wave's copies of tile k have landed
             } else {
                 wait_vmcnt<0>();
             }
@@ -604,7 +611,8 @@ template <int D, int BLK, int RTW, int NW>
 hipError_t launch_bf16(const RectifyParams& p, hipStream_t stream) {
     constexpr int RWG = 16 * RTW * NW;
     if (p.a.rows_per_wg != RWG) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((rectify_bf16_kernel<D, BLK, RTW, kStages, NW>), dim3(p.a.wgs),
+    constexpr int NS = (RTW == 2) ? BSA_RECTIFY_STAGES_WIDE : kStages;
+    hipLaunchKernelGGL((rectify_bf16_kernel<D, BLK, RTW, NS, NW>), dim3(p.a.wgs),
                        dim3(NW * kWave), 0, stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
