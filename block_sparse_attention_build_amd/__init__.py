@@ -122,6 +122,12 @@ def _need(t, name, dtype, numel):
     """t must be a contiguous GPU tensor of `dtype` (None: any) with at least
     `numel` elements: the library reaches it through its data pointer alone,
     so a wrong tensor is refused here rather than read out of bounds."""
+    try:  # the common case in one expression: a few attribute reads per call
+        if (t.is_cuda and (dtype is None or t.dtype == dtype) and t.is_contiguous()
+                and t.numel() >= numel):
+            return
+    except AttributeError:
+        pass
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a torch tensor, got {type(t).__name__}")
