@@ -433,6 +433,11 @@ def summarize(w, bp, layers, m):
          "decode_kernel_us": round(m["decode_us_avg"], 2),
          "decode_GBps": round(m["decode_kv_bytes_per_call"] / (m["decode_us_avg"] * 1e-6) / 1e9, 1),
          "bytes_per_step_layer": int(gm["eff_bytes_per_step_layer"])}
+    if not w.rectify_f:
+        # the step's time outside the decode call: append + scoring + top-n
+        sel = gm["us_per_step_layer"] - m["decode_us_avg"]
+        s["select_us"] = round(sel, 2)
+        s["select_share"] = round(sel / gm["us_per_step_layer"], 3)
     if "rectify" in m:
         r = m["rectify"]
         s["rectify"] = {"us_per_call": round(r["us_avg"], 1),
