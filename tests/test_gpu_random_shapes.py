@@ -1,8 +1,8 @@
-"""Select + decode, and rectify, against the oracle on seeded random shapes:
-batch, KV heads, group size, head dim, block size, ragged lengths (down to
-one token), budget or sparsity, local and minimum counts, descriptor kind,
-KV dtype and the rectify interval f are drawn per case, so combinations no
-hand-written case names are covered too.  Same bars as the other parity
+"""Select + decode (plain and with the log-gate bias), and rectify, against
+the oracle on seeded random shapes: batch, KV heads, group size, head dim,
+block size, ragged lengths (down to one token), budget or sparsity, local
+and minimum counts, descriptor kind, KV dtype and the rectify interval f are
+drawn per case, so combinations no hand-written case names are covered too.  Same bars as the other parity
 tests: selection bit-exact (inputs carry the score gap), o within 2e-2
 (1e-4 for fp32 rectify), lse within 1e-4 relative, and the rectified cache
 and descriptors exact."""
@@ -13,11 +13,13 @@ import block_sparse_attention_build_amd as bsa
 from harness import compare_step, enforce_gap, oracle_decode, prefill, random_page_table, to_dev
 from test_gpu_parity import BF16, F32, MEAN, MINMAX, make_inputs, run_select_decode
 from test_gpu_parity import test_rectify_parity as rectify_case
+from test_gpu_gate import test_gated_select_decode_parity as gated_case
 
 pytestmark = pytest.mark.gpu
 
 N_CASES = 64
 N_RECTIFY = 16
+N_GATED = 16
 
 
 def _draw(seed):
@@ -82,3 +84,12 @@ def test_random_shape_rectify(seed):
     case = _draw_rectify(seed)
     print(f"seed {seed}: {case}", flush=True)
     rectify_case(*case)
+
+
+@pytest.mark.parametrize("seed", range(N_GATED))
+def test_random_shape_gated_select_decode(seed):
+    """The same draws with the log-gate bias: bias beside each kept id and the
+    gated decode, against the oracle."""
+    case = _draw(1000 + seed)
+    print(f"seed {1000 + seed}: {case}", flush=True)
+    gated_case(case)
