@@ -141,6 +141,19 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
         const int j = min(c0 + (it * (kScoreThreads / kWave) + wave) * BPL + bl, c.max_blocks - 1);
         Chunk<DE>::load(base + static_cast<int64_t>(j) * Gm::BR, x[it]);
     }
+    // mean-pool: this thread's share of a gate matrix row, requested with
+    // the descriptors (it depends on nothing else), so that the product
+    // w = W u below waits for no second round trip
+    constexpr int PARTS = kScoreThreads / D;
+    constexpr int KP = D / PARTS;
+    static_assert(PARTS * D == kScoreThreads && KP % 8 == 0, "gate matvec split");
+    u32x4 wl[KP / 8];
+    if (DESC == kMeanPool) {
+        const uint16_t* wr =
+            static_cast<const uint16_t*>(a.gate_w) + (tid % D) * D + (tid / D) * KP;
+#pragma unroll
+        for (int k = 0; k < KP / 8; ++k) wl[k] = *reinterpret_cast<const u32x4*>(wr + 8 * k);
+    }
     // 2. the group's query weights, once per workgroup, into LDS:
     //    min/max: Q-_i = sum_h min(q_hi, 0) (pairs with the min row) and
     //             Q+_i = sum_h max(q_hi, 0) (pairs with the max row);
@@ -179,21 +192,13 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
         for (int e = 0; e < EPL; ++e) wv[e] = src[e];
     } else {
         // w = W u in LDS: kScoreThreads / D threads per output channel, each
-        // a 16-byte-load dot product over its share of the row, then the
+        // a dot product over its share of the row (loaded above), then the
         // shares added in fixed order
-        constexpr int PARTS = kScoreThreads / D;
-        constexpr int KP = D / PARTS;
-        static_assert(PARTS * D == kScoreThreads && KP % 8 == 0, "gate matvec split");
         const float* u_s = qw;
         __shared__ float w_part[kScoreThreads];
         __shared__ float w_s[D];
         {
-            const int r = tid % D;
             const int part = tid / D;
-            const uint16_t* wr = static_cast<const uint16_t*>(a.gate_w) + r * D + part * KP;
-            u32x4 wl[KP / 8];
-#pragma unroll
-            for (int k = 0; k < KP / 8; ++k) wl[k] = *reinterpret_cast<const u32x4*>(wr + 8 * k);
             float acc = 0.f;
 #pragma unroll
             for (int k = 0; k < KP / 8; ++k)
