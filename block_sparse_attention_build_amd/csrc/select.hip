@@ -141,18 +141,22 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
         const int j = min(c0 + (it * (kScoreThreads / kWave) + wave) * BPL + bl, c.max_blocks - 1);
         Chunk<DE>::load(base + static_cast<int64_t>(j) * Gm::BR, x[it]);
     }
-    // mean-pool: this thread's share of a gate matrix row, requested with
-    // the descriptors (it depends on nothing else), so that the product
-    // w = W u below waits for no second round trip
-    constexpr int PARTS = kScoreThreads / D;
-    constexpr int KP = D / PARTS;
-    static_assert(PARTS * D == kScoreThreads && KP % 8 == 0, "gate matvec split");
-    u32x4 wl[KP / 8];
+    // mean-pool: the gate matrix (row-major bf16), requested with the
+    // descriptors since it depends on nothing else.  It is read in 16-byte
+    // pieces, LPR lanes per row, so that every wave load covers whole rows.
+    constexpr int LPR = D / 8;                    // lanes per gate row
+    constexpr int RPI = kWave / LPR;              // rows per wave load
+    constexpr int NWV = kScoreThreads / kWave;    // waves per workgroup
+    constexpr int NI = D / (NWV * RPI);           // loads per thread
+    static_assert(NI * NWV * RPI == D, "gate matrix split");
+    u32x4 wl[NI];
     if (DESC == kMeanPool) {
-        const uint16_t* wr =
-            static_cast<const uint16_t*>(a.gate_w) + (tid % D) * D + (tid / D) * KP;
+        const uint16_t* wg = static_cast<const uint16_t*>(a.gate_w) + (lane % LPR) * 8;
 #pragma unroll
-        for (int k = 0; k < KP / 8; ++k) wl[k] = *reinterpret_cast<const u32x4*>(wr + 8 * k);
+        for (int k = 0; k < NI; ++k) {
+            const int r = (k * NWV + wave) * RPI + lane / LPR;
+            wl[k] = *reinterpret_cast<const u32x4*>(wg + r * D);
+        }
     }
     // 2. the group's query weights, once per workgroup, into LDS:
     //    min/max: Q-_i = sum_h min(q_hi, 0) (pairs with the min row) and
@@ -191,30 +195,33 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
 #pragma unroll
         for (int e = 0; e < EPL; ++e) wv[e] = src[e];
     } else {
-        // w = W u in LDS: kScoreThreads / D threads per output channel, each
-        // a dot product over its share of the row (loaded above), then the
-        // shares added in fixed order
-        const float* u_s = qw;
-        __shared__ float w_part[kScoreThreads];
+        // w = W u in LDS: each lane forms the 8-channel piece of the rows
+        // it loaded above, then the LPR pieces of a row are added in
+        // channel order (rows padded by one float against bank conflicts)
+        __shared__ float w_part[D * (LPR + 1)];
         __shared__ float w_s[D];
         {
-            const int part = tid / D;
-            float acc = 0.f;
+            const int j = lane % LPR;
+            float uv[8];
 #pragma unroll
-            for (int k = 0; k < KP / 8; ++k)
+            for (int e = 0; e < 8; ++e) uv[e] = qw[8 * j + e];
+#pragma unroll
+            for (int k = 0; k < NI; ++k) {
+                const int r = (k * NWV + wave) * RPI + lane / LPR;
+                float acc = 0.f;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float* uu = u_s + part * KP + 8 * k + 2 * e;
-                    acc += __uint_as_float(wl[k][e] << 16) * uu[0];
-                    acc += __uint_as_float(wl[k][e] & 0xffff0000u) * uu[1];
+                    acc += __uint_as_float(wl[k][e] << 16) * uv[2 * e];
+                    acc += __uint_as_float(wl[k][e] & 0xffff0000u) * uv[2 * e + 1];
                 }
-            w_part[tid] = acc;
+                w_part[r * (LPR + 1) + j] = acc;
+            }
         }
         __syncthreads();
         if (tid < D) {
             float acc = 0.f;
 #pragma unroll
-            for (int pp = 0; pp < PARTS; ++pp) acc += w_part[pp * D + tid];
+            for (int jj = 0; jj < LPR; ++jj) acc += w_part[tid * (LPR + 1) + jj];
             w_s[tid] = acc;
         }
         __syncthreads();
