@@ -75,6 +75,11 @@ struct DecodeParams {
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
+// K and V tiles are read once per call: streaming (nontemporal) loads keep
+// them from displacing reused lines in L2 and the last-level cache
+__device__ __forceinline__ u32x4 ldg16_stream(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 
 // Merge the per-wave (m, l, O) held in LDS and write one partial per head.
 // sm/sl: [kWaves][16]; so: [kWaves][G][D].
@@ -216,11 +221,11 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     };
     auto load_k = [&](int64_t off) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < 2 * KS; ++k) kr[k] = ldg16(kl + off + k * 512);
+        for (int k = 0; k < 2 * KS; ++k) kr[k] = ldg16_stream(kl + off + k * 512);
     };
     auto load_v = [&](int64_t off) __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < NT; ++n) vr[n] = ldg16(vl + off + n * 512);
+        for (int n = 0; n < NT; ++n) vr[n] = ldg16_stream(vl + off + n * 512);
     };
     // one tile: QK, online softmax, PV; NEXT: also issue the next tile's loads
     auto step = [&](const int nvalid, const float b2, const bool next, const int64_t off_nxt)
