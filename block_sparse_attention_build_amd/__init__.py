@@ -27,8 +27,10 @@ DESC_MINMAX, DESC_MEANPOOL = 0, 1
 OP_SELECT, OP_DECODE, OP_RECTIFY = 1, 2, 3
 
 EXPORTS = ("bsa_build_block_desc", "bsa_select_blocks", "bsa_append_select",
-           "bsa_sparse_decode", "bsa_sparse_decode_gated", "bsa_rectify_chunk",
-           "bsa_workspace_size", "bsa_block_count", "bsa_status_string")
+           "bsa_sparse_decode", "bsa_sparse_decode_gated", "bsa_sparse_decode_static",
+           "bsa_rectify_chunk", "bsa_workspace_size", "bsa_block_count", "bsa_status_string")
+# bytes of the library's per-GPU scratch array (bsa_sparse_decode_static)
+STATIC_SCRATCH_BYTES = 16 << 20
 
 
 class BsaError(RuntimeError):
@@ -75,6 +77,7 @@ def lib():
     L.bsa_sparse_decode.argtypes = [pl, pc, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     L.bsa_sparse_decode_gated.argtypes = [pl, pc, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp,
                                           vp, sz, vp]
+    L.bsa_sparse_decode_static.argtypes = [pl, pc, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp]
     L.bsa_rectify_chunk.argtypes = [pl, pc, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     L.bsa_workspace_size.argtypes = [pl, i32, i32]
     L.bsa_workspace_size.restype = sz
@@ -83,7 +86,8 @@ def lib():
     L.bsa_status_string.argtypes = [ctypes.c_int]
     L.bsa_status_string.restype = ctypes.c_char_p
     for fn in (L.bsa_build_block_desc, L.bsa_select_blocks, L.bsa_append_select,
-               L.bsa_sparse_decode, L.bsa_sparse_decode_gated, L.bsa_rectify_chunk):
+               L.bsa_sparse_decode, L.bsa_sparse_decode_gated, L.bsa_sparse_decode_static,
+               L.bsa_rectify_chunk):
         fn.restype = ctypes.c_int
     _lib = L
     return L
@@ -175,7 +179,8 @@ def _need_decode(L, cache, q, idx, cnt, n_max, o, lse, ws):
     _need(cnt, "cnt", torch.int32, L.B * L.Hkv)
     _need(o, "o", L.torch_dtype(), L.B * L.Hq * L.d)
     _need(lse, "lse", torch.float32, L.B * L.Hq)
-    _need(ws, "ws", None, 0)
+    if ws is not None:
+        _need(ws, "ws", None, 0)
 
 
 # ---------------------------------------------------------------------------
@@ -339,6 +344,18 @@ def sparse_decode_gated(layout: Layout, cache: Cache, q, idx, cnt, gate_bias, n_
                                        float(softmax_scale), _ptr(o), _ptr(lse), _ptr(ws),
                                        ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "bsa_sparse_decode_gated")
+
+
+def sparse_decode_static(layout: Layout, cache: Cache, q, idx, cnt, n_max: int,
+                         softmax_scale: float, o, lse, stream=None):
+    """sparse_decode with the split partials in the library's per-GPU
+    scratch array instead of a caller workspace (no allocation anywhere;
+    calls that overlap on one GPU race)."""
+    _need_decode(layout, cache, q, idx, cnt, n_max, o, lse, None)
+    st = lib().bsa_sparse_decode_static(ctypes.byref(layout.c()), ctypes.byref(cache.c()),
+                                        _ptr(q), _ptr(idx), _ptr(cnt), int(n_max),
+                                        float(softmax_scale), _ptr(o), _ptr(lse), _stream(stream))
+    _check(st, "bsa_sparse_decode_static")
 
 
 def rectify_chunk(layout: Layout, cache: Cache, q, k_new, v_new, f: int, softmax_scale: float,

@@ -12,6 +12,9 @@
 #include <math.h>
 #include <stddef.h>
 
+#include <atomic>
+#include <mutex>
+
 #ifndef BSA_CHECKED
 #define BSA_CHECKED 0
 #endif
@@ -25,7 +28,35 @@
 
 using namespace bsa;
 
+// Scratch memory of bsa_sparse_decode_static: one copy of this array per GPU,
+// held until the process ends.  In host code `scratch` is only a stand-in
+// for the symbol: its device address (per device) comes from
+// hipGetSymbolAddress, and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[BSA_STATIC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+
+// The device address of the current device's copy of `scratch`, resolved on
+// the first call on that device (with that device current) and kept.
+bsa_status static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return BSA_ERR_HIP;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return BSA_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return BSA_OK;
+}
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -197,16 +228,26 @@ bsa_status contract_kept(const CacheArgs&, const int32_t*, const int32_t*, const
 }
 #endif
 
+// Host-side checks of a decode call, workspace aside.
+bsa_status check_decode(const bsa_layout* layout, const bsa_cache* cache, const void* q,
+                        const int32_t* idx, const int32_t* cnt, int32_t n_max,
+                        float softmax_scale, const void* o, const float* lse) {
+    bsa_status st = check_layout(layout);
+    if (st != BSA_OK) return st;
+    if ((st = check_cache(cache)) != BSA_OK) return st;
+    if (!q || !idx || !cnt || !o || !lse) return BSA_ERR_NULL;
+    if (n_max < 1 || n_max > layout->max_blocks) return BSA_ERR_PARAM;
+    if (!scale_ok(softmax_scale)) return BSA_ERR_PARAM;
+    return BSA_OK;
+}
+
 bsa_status sparse_decode(const bsa_layout* layout, const bsa_cache* cache, const void* q,
                          const int32_t* idx, const int32_t* cnt, const float* bias, int32_t n_max,
                          float softmax_scale, void* o, float* lse, void* ws, size_t ws_bytes,
                          hipStream_t stream) {
-    bsa_status st = check_layout(layout);
+    bsa_status st = check_decode(layout, cache, q, idx, cnt, n_max, softmax_scale, o, lse);
     if (st != BSA_OK) return st;
-    if ((st = check_cache(cache)) != BSA_OK) return st;
-    if (!q || !idx || !cnt || !o || !lse || !ws) return BSA_ERR_NULL;
-    if (n_max < 1 || n_max > layout->max_blocks) return BSA_ERR_PARAM;
-    if (!scale_ok(softmax_scale)) return BSA_ERR_PARAM;
+    if (!ws) return BSA_ERR_NULL;
     const CacheArgs c = make_args(layout, cache);
     const DecodeWs w = decode_ws(c, n_max);
     if (ws_bytes < w.total) return BSA_ERR_WORKSPACE;
@@ -357,6 +398,20 @@ bsa_status bsa_sparse_decode_gated(const bsa_layout* layout, const bsa_cache* ca
     if (!gate_bias) return BSA_ERR_NULL;
     return sparse_decode(layout, cache, q, idx, cnt, gate_bias, n_max, softmax_scale, o, lse, ws,
                          ws_bytes, stream);
+}
+
+bsa_status bsa_sparse_decode_static(const bsa_layout* layout, const bsa_cache* cache,
+                                    const void* q, const int32_t* idx, const int32_t* cnt,
+                                    int32_t n_max, float softmax_scale, void* o, float* lse,
+                                    hipStream_t stream) {
+    bsa_status st = check_decode(layout, cache, q, idx, cnt, n_max, softmax_scale, o, lse);
+    if (st != BSA_OK) return st;
+    if (decode_ws(make_args(layout, cache), n_max).total > BSA_STATIC_SCRATCH_BYTES)
+        return BSA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if ((st = static_scratch(&ws)) != BSA_OK) return st;
+    return sparse_decode(layout, cache, q, idx, cnt, nullptr, n_max, softmax_scale, o, lse, ws,
+                         BSA_STATIC_SCRATCH_BYTES, stream);
 }
 
 bsa_status bsa_rectify_chunk(const bsa_layout* layout, const bsa_cache* cache, const void* q,

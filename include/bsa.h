@@ -29,8 +29,10 @@
  * Ownership.  The caller allocates every buffer (device memory unless stated):
  *   pools, page table, sequence lengths, descriptors, selection lists,
  *   outputs and workspace.  The library allocates nothing, frees nothing and
- *   keeps no state between calls.  Pointers must stay valid until the work
- *   enqueued on `stream` has completed.
+ *   keeps no state between calls (the one exception is the per-GPU scratch
+ *   array of bsa_sparse_decode_static, a device variable of fixed size that
+ *   the library's code object holds).  Pointers must stay valid until the
+ *   work enqueued on `stream` has completed.
  * Streams.  Every call validates its arguments on the host, enqueues kernels
  *   on `stream` (0 = the null stream) and returns.  The library never
  *   synchronises.  Calls on one cache must be ordered by the caller (the
@@ -293,6 +295,34 @@ BSA_API bsa_status bsa_sparse_decode_gated(const bsa_layout* layout,
                              const float* gate_bias, int32_t n_max,
                              float softmax_scale, void* o, float* lse,
                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * bsa_sparse_decode_static -- bsa_sparse_decode without a workspace
+ * argument, for callers that cannot allocate device memory around the call
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The split partials go to a scratch array of
+ * BSA_STATIC_SCRATCH_BYTES that the library holds in a file-scope device
+ * variable: one copy per GPU, kept until the process ends.  The call
+ * allocates nothing and frees nothing; on its first use on a device (with
+ * that device current) it looks up the device address of that device's
+ * copy once.  `stream` must belong to the current device.
+ * Results are bit-identical to bsa_sparse_decode with the same arguments.
+ * Every call on one GPU shares that GPU's scratch array, and the array keeps
+ * the last call's contents: calls whose work may overlap on one GPU (other
+ * streams, other host threads) race and give undefined results; order them
+ * on one stream.  Nothing in the array needs to start at zero.
+ * Arguments as in bsa_sparse_decode.
+ * Errors: as bsa_sparse_decode; BSA_ERR_WORKSPACE when the call needs more
+ *   than BSA_STATIC_SCRATCH_BYTES (bsa_workspace_size(layout, BSA_OP_DECODE,
+ *   n_max) > BSA_STATIC_SCRATCH_BYTES; use bsa_sparse_decode with a caller
+ *   workspace then); BSA_ERR_HIP if the scratch address cannot be looked up.
+ * ------------------------------------------------------------------------- */
+#define BSA_STATIC_SCRATCH_BYTES (16u << 20)
+BSA_API bsa_status bsa_sparse_decode_static(const bsa_layout* layout,
+                             const bsa_cache* cache, const void* q,
+                             const int32_t* idx, const int32_t* cnt,
+                             int32_t n_max, float softmax_scale, void* o,
+                             float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * bsa_rectify_chunk -- ReSA rectification of the last f tokens of every

@@ -274,3 +274,24 @@ def test_binding_refuses_host_tensors_and_non_tensors():
     C_list = bsa.Cache([0.0], C.v_pool, C.page_table, C.seq_lens, C.desc)
     with pytest.raises(TypeError, match="torch tensor"):
         bsa.sparse_decode(L, C_list, q, idx, cnt, 2, 0.125, o, lse, ws)
+
+
+def test_static_scratch_decode_validates_before_any_hip_call():
+    # the decode without a workspace refuses a call whose split partials
+    # exceed the library's scratch array, and bad arguments, on the host
+    fake = ctypes.c_void_p(0x1000)
+    C = bsa.c_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    big = L_ok(B=256, Hq=128, Hkv=8, max_blocks=64)
+    assert bsa.workspace_size(big, bsa.OP_DECODE, 16) > bsa.STATIC_SCRATCH_BYTES
+    f = bsa.lib().bsa_sparse_decode_static
+    assert f(ctypes.byref(big.c()), ctypes.byref(C), fake, fake, fake, 16, 0.1, fake, fake,
+             None) == bsa.ERR_WORKSPACE
+    L = L_ok()
+    assert f(ctypes.byref(L.c()), ctypes.byref(C), None, fake, fake, 10, 0.1, fake, fake,
+             None) == bsa.ERR_NULL
+    assert f(ctypes.byref(L.c()), ctypes.byref(C), fake, fake, fake, 0, 0.1, fake, fake,
+             None) == bsa.ERR_PARAM
+    assert f(ctypes.byref(L.c()), ctypes.byref(C), fake, fake, fake, 10, -1.0, fake, fake,
+             None) == bsa.ERR_PARAM
+    assert f(ctypes.byref(L_ok(d=96).c()), ctypes.byref(C), fake, fake, fake, 10, 0.1, fake,
+             fake, None) == bsa.ERR_UNSUPPORTED
