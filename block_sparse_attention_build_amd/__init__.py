@@ -54,7 +54,8 @@ class c_select_params(ctypes.Structure):
     _fields_ = [("budget_tokens", ctypes.c_int32), ("sparsity_bp", ctypes.c_int32),
                 ("n_local", ctypes.c_int32), ("n_min", ctypes.c_int32),
                 ("n_max", ctypes.c_int32), ("gate_w", ctypes.c_void_p),
-                ("gate_tau", ctypes.c_float), ("gate_bias", ctypes.c_void_p)]
+                ("gate_tau", ctypes.c_float), ("gate_bias", ctypes.c_void_p),
+                ("gate_current", ctypes.c_int32)]
 
 
 _lib = None
@@ -221,12 +222,14 @@ class SelectParams:
     gate_w: Optional[object] = None  # torch bf16 [d, d] on the device
     gate_tau: float = 0.0
     gate_bias: Optional[object] = None  # torch fp32 [B, Hkv, n_max] on the device, OUT
+    gate_current: int = 1  # trailing blocks with the unit gate (the page's current block: 1)
 
     def c(self):
         return c_select_params(self.budget_tokens, self.sparsity_bp, self.n_local, self.n_min,
                                self.n_max, None if self.gate_w is None else self.gate_w.data_ptr(),
                                float(self.gate_tau),
-                               None if self.gate_bias is None else self.gate_bias.data_ptr())
+                               None if self.gate_bias is None else self.gate_bias.data_ptr(),
+                               int(self.gate_current))
 
 
 @dataclass

@@ -147,6 +147,7 @@ bsa_status check_select_params(const bsa_layout* L, const bsa_select_params* P) 
                                  P->n_local, P->n_min);
     if (P->n_max < need) return BSA_ERR_PARAM;
     if (P->gate_bias && !(isfinite(P->gate_tau) && P->gate_tau >= 0.f)) return BSA_ERR_PARAM;
+    if (P->gate_bias && (P->gate_current < 0 || P->gate_current > P->n_local)) return BSA_ERR_PARAM;
     return BSA_OK;
 }
 
@@ -350,6 +351,7 @@ bsa_status bsa_select_blocks(const bsa_layout* layout, const bsa_cache* cache, c
     s.scores = static_cast<float*>(ws);
     s.gate_tau = params->gate_tau;
     s.gate_bias = params->gate_bias;
+    s.gate_current = params->gate_current > 1 ? params->gate_current : 1;
     return hip_status(launch_select(c, s, stream));
 }
 
@@ -379,6 +381,7 @@ bsa_status bsa_append_select(const bsa_layout* layout, const bsa_cache* cache, c
     s.scores = static_cast<float*>(ws);
     s.gate_tau = params->gate_tau;
     s.gate_bias = params->gate_bias;
+    s.gate_current = params->gate_current > 1 ? params->gate_current : 1;
     return hip_status(launch_append_select(c, k_new, v_new, s, stream));
 }
 

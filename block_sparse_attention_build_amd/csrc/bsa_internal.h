@@ -35,6 +35,7 @@ struct SelectArgs {
     float* scores;  // workspace [B*Hkv][score_stride(max_blocks)]
     float gate_tau;
     float* gate_bias;  // nullptr, or [B*Hkv][n_max]: log-gate bias per idx entry
+    int gate_current;  // with gate_bias: trailing blocks with the unit gate (>= 1)
 };
 hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t stream);
 // Append of one token per sequence (kModeAppend, n_new = 1) and selection,

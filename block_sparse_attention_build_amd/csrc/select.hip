@@ -185,8 +185,9 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
     }
     const int T = c.seq_lens[s];
     const int NB = (T + c.block - 1) / c.block;
-    const int nl = min(a.n_local, NB);
-    const int NC = NB - nl;
+    // scored: the candidates, and with a log-gate bias every historical
+    // block (all but the gate_current trailing ones, kept local ones included)
+    const int NC = NB - min(a.gate_bias ? a.gate_current : a.n_local, NB);
     __syncthreads();
     if (c0 >= NC) return;  // uniform across the workgroup
     float wv[EPL];
@@ -292,6 +293,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     __shared__ uint32_t res_s[2];
     __shared__ uint32_t red_min[kTopnWaves], red_max[kTopnWaves];
     __shared__ float red_z[kTopnWaves];
+    __shared__ float red_x[kTopnWaves];  // largest extra historical score per wave
     __shared__ uint32_t w0keys[KPT * kWave];  // wave 0's keys, slot r * 64 + lane
 
     const int grp = blockIdx.x;
@@ -354,10 +356,16 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     // Only picked candidates carry a bias, so with nothing picked there is
     // no normaliser to form.
     float* bias_out = a.gate_bias ? a.gate_bias + static_cast<int64_t>(grp) * a.n_max : nullptr;
-    const bool gated = bias_out != nullptr && mode != 0;  // uniform
     const float tau_l2 = a.gate_tau * kLog2e;
     float g_smax = 0.f, g_lnz = 0.f;
-    // this wave's part of sum_c exp(tau * (s_c - smax)), into red_z[wave]
+    // Historical blocks past the candidates: the kept local blocks before the
+    // gate_current current ones.  They are scored (after the candidates in
+    // the score row), enter the normaliser and carry their own log-gate;
+    // thread t handles extras t, t + 1024, ... (usually none or one).
+    const int n_extra = bias_out ? max(0, nl - min(a.gate_current, NB)) : 0;
+    // a normaliser is needed when some kept block is historical
+    const bool gated = bias_out != nullptr && (mode != 0 || n_extra > 0);  // uniform
+    // this wave's part of sum_h exp(tau * (s_h - smax)), into red_z[wave]
     auto gate_sum_part = [&]() __attribute__((always_inline)) {
         float z = 0.f;
         if (live) {
@@ -366,8 +374,16 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
                 if (key[r] != 0u)
                     z += __builtin_amdgcn_exp2f(tau_l2 * (key_float(key[r]) - g_smax));
         }
+        for (int e = tid; e < n_extra; e += kTopnThreads)
+            z += __builtin_amdgcn_exp2f(tau_l2 * (sc[NC + e] - g_smax));
         z = wave_sum(z);
         if (lane == 0) red_z[wave] = z;
+    };
+    // the largest extra score of this thread (-inf if none), for smax
+    auto extra_max = [&]() __attribute__((always_inline)) {
+        float m = -INFINITY;
+        for (int e = tid; e < n_extra; e += kTopnThreads) m = fmaxf(m, sc[NC + e]);
+        return m;
     };
     // wave 0's part, formed by another wave from w0keys (the same terms in
     // the same order as wave 0 would add them)
@@ -378,6 +394,9 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
             const uint32_t k = w0keys[r * kWave + lane];
             if (k != 0u) z += __builtin_amdgcn_exp2f(tau_l2 * (key_float(k) - g_smax));
         }
+        // and the extras wave 0's threads hold
+        for (int e = lane; e < n_extra; e += kTopnThreads)
+            z += __builtin_amdgcn_exp2f(tau_l2 * (sc[NC + e] - g_smax));
         z = wave_sum(z);
         if (lane == 0) red_z[0] = z;
     };
@@ -391,24 +410,26 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         return a.gate_tau * (key_float(k) - g_smax) - g_lnz;
     };
 
-    if (mode == 1) {
-        if (gated) {
-            uint32_t lmax = 0u;
-            if (live) {
+    if (mode != 2 && gated) {
+        uint32_t lmax = 0u;
+        if (live) {
 #pragma unroll
-                for (int r = 0; r < KPT; ++r) lmax = max(lmax, key[r]);
-            }
-            lmax = wave_max_u32(lmax);
-            if (lane == 0) red_max[wave] = lmax;
-            __syncthreads();
-            uint32_t kmx = 0u;
-#pragma unroll
-            for (int w = 0; w < kTopnWaves; ++w) kmx = max(kmx, red_max[w]);
-            g_smax = key_float(kmx);
-            gate_sum_part();
-            __syncthreads();
-            gate_finish();
+            for (int r = 0; r < KPT; ++r) lmax = max(lmax, key[r]);
         }
+        const float xm = extra_max();
+        if (xm != -INFINITY) lmax = max(lmax, float_key(xm));
+        lmax = wave_max_u32(lmax);
+        if (lane == 0) red_max[wave] = lmax;
+        __syncthreads();
+        uint32_t kmx = 0u;
+#pragma unroll
+        for (int w = 0; w < kTopnWaves; ++w) kmx = max(kmx, red_max[w]);
+        g_smax = key_float(kmx);
+        gate_sum_part();
+        __syncthreads();
+        gate_finish();
+    }
+    if (mode == 1) {
         if (live) {
 #pragma unroll
             for (int r = 0; r < KPT; ++r) {
@@ -433,19 +454,24 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         }
         lmin = wave_min_u32(lmin);
         lmax = wave_max_u32(lmax);
+        // the normaliser's maximum also covers the extra historical blocks
+        const float xm = gated ? wave_max(extra_max()) : -INFINITY;
         if (lane == 0) {
             red_min[wave] = lmin;
             red_max[wave] = lmax;
+            red_x[wave] = xm;
         }
         __syncthreads();
         uint32_t kmin = 0xffffffffu, kmax = 0u;
+        float xmax = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kTopnWaves; ++w) {
             kmin = min(kmin, red_min[w]);
             kmax = max(kmax, red_max[w]);
+            xmax = fmaxf(xmax, red_x[w]);
         }
         kmin += 1u;
-        g_smax = key_float(kmax);
+        g_smax = fmaxf(key_float(kmax), xmax);
         bool z_pending = gated;  // the normaliser's parts are still to form
         const uint32_t range = kmax - kmin;
         uint32_t prefix = 0;  // of key - kmin, above the current digit
@@ -653,8 +679,16 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     // local blocks follow the picked candidates (their ids are the largest)
     for (int t = tid; t < nl; t += kTopnThreads) out[picked + t] = NC + t;
     for (int t = picked + nl + tid; t < a.n_max; t += kTopnThreads) out[t] = -1;
-    if (bias_out)
-        for (int t = picked + tid; t < a.n_max; t += kTopnThreads) bias_out[t] = 0.f;
+    if (bias_out) {
+        // the extra historical blocks lead the local blocks; the current
+        // blocks and the padding get 0
+        for (int t = picked + tid; t < a.n_max; t += kTopnThreads) {
+            const int e = t - picked;
+            bias_out[t] = (e < n_extra)
+                              ? a.gate_tau * (sc[NC + e] - g_smax) - g_lnz
+                              : 0.f;
+        }
+    }
     if (tid == 0) a.cnt[grp] = picked + nl;
 }
 

@@ -157,14 +157,20 @@ typedef struct bsa_cache {
  * The last min(n_local, NB) blocks are always kept; the rest of the n are
  * the best-scoring other blocks, ties to the lower block index.
  *
- * Log-gate bias ("Simple Attention Sparsification", Method: gates are a
- * softmax over all candidate blocks' scores, the current block's gate is 1,
- * and log g is added to a kept block's logits).  When gate_bias is set, the
- * selecting call also writes, at the position of each kept block j in idx,
- *   bias = log softmax(gate_tau * s)_j   over ALL C = NB - n_local candidates,
- * 0 for a local block and 0 for the -1 padding; computed in fp32 from the
- * fp32 scores as gate_tau * (s_j - max s) - ln sum_c exp(gate_tau * (s_c -
- * max s)).  bsa_sparse_decode_gated consumes it. */
+ * Log-gate bias ("Simple Attention Sparsification", Method: the context is
+ * one always-retained current block, whose gate is 1, and historical
+ * blocks, whose gates are a softmax over all their scores; log g is added to
+ * a kept block's logits).  The last gate_current blocks are current (1, the
+ * page's single current block, when gate_current is 0 or 1; at most
+ * n_local); every other block is historical and is scored, a kept local one
+ * included.  When gate_bias is set, the selecting call also writes, at the
+ * position of each kept block j in idx,
+ *   bias = log softmax(gate_tau * s)_j  over ALL H = NB - gate_current
+ *          historical blocks,
+ * 0 for a current block and 0 for the -1 padding; computed in fp32 from the
+ * fp32 scores as gate_tau * (s_j - max s) - ln sum_h exp(gate_tau * (s_h -
+ * max s)).  bsa_sparse_decode_gated consumes it.  The selection itself
+ * (which blocks are kept) does not depend on the gate settings. */
 typedef struct bsa_select_params {
     int32_t budget_tokens;  /* >= 0; 0 selects the sparsity rule */
     int32_t sparsity_bp;    /* p (fraction skipped) in basis points, [0, 10000) */
@@ -176,6 +182,8 @@ typedef struct bsa_select_params {
     float gate_tau;         /* >= 0, finite; read only when gate_bias is set */
     float* gate_bias;       /* NULL, or device fp32 [B][Hkv][n_max], OUT: the
                                log-gate bias of each entry of idx (below) */
+    int32_t gate_current;   /* read only when gate_bias is set: trailing
+                               blocks with the unit gate, 0..n_local (0 = 1) */
 } bsa_select_params;
 
 /* ---------------------------------------------------------------------------
@@ -228,7 +236,8 @@ BSA_API bsa_status bsa_build_block_desc(const bsa_layout* layout, const bsa_cach
  * Errors: BSA_ERR_NULL, BSA_ERR_SHAPE, BSA_ERR_UNSUPPORTED, BSA_ERR_PARAM
  *   (n_local < 1, n_min < 0, budget_tokens < 0, sparsity_bp outside
  *   [0, 10000), n_max too small, gate_w missing for MEANPOOL, gate_tau
- *   negative or not finite while gate_bias is set),
+ *   negative or not finite or gate_current outside [0, n_local] while
+ *   gate_bias is set),
  *   BSA_ERR_WORKSPACE, BSA_ERR_HIP.
  * ------------------------------------------------------------------------- */
 BSA_API bsa_status bsa_select_blocks(const bsa_layout* layout, const bsa_cache* cache,

@@ -60,7 +60,7 @@ def lib():
                                     _i64, _f64p, ctypes.c_double, _f64p, _f64p]
     L.orc_decode_group_gated.argtypes = [_f32p, _int, _f32p, _f32p, _i64, _int,
                                          _int, _int, _f32p, _i64, _int, _int, _int,
-                                         ctypes.c_double, ctypes.c_double, _i32p,
+                                         _int, ctypes.c_double, ctypes.c_double, _i32p,
                                          _i64, _f64p, _f64p, _f64p]
     L.orc_decode_group_gated.restype = _i64
     _LIB = L
@@ -216,16 +216,16 @@ def decode_group(q, K, V, b, desc_kind, W=None, budget_tokens=0, sparsity_bp=0,
     return out
 
 
-def gate_bias(scores, NB, n_local, tau, idx):
+def gate_bias(scores, NB, n_current, tau, idx):
     """Log-gate bias (SAS) of the selected blocks idx: log softmax(tau * s)
-    over the NB - n_local candidates, 0 for the local blocks.
-    scores: [>= NB - n_local] candidate scores."""
+    over the NB - n_current historical blocks, 0 for the n_current trailing
+    (current) blocks.  scores: [>= NB - n_current] historical-block scores."""
     full = np.full(max(NB, 1), np.nan, np.float64)
     sc = np.asarray(scores, np.float64)
     full[: min(sc.shape[0], NB)] = sc[: NB]
     idx = np.ascontiguousarray(idx, dtype=np.int32)
     bias = np.empty(max(idx.shape[0], 1), np.float64)
-    lib().orc_gate_bias(full.ctypes.data_as(_f64p), NB, n_local, tau,
+    lib().orc_gate_bias(full.ctypes.data_as(_f64p), NB, n_current, tau,
                         idx.ctypes.data_as(_i32p), idx.shape[0],
                         bias.ctypes.data_as(_f64p))
     return bias[: idx.shape[0]].copy()
@@ -249,8 +249,9 @@ def attend_biased(q, K, V, b, idx, bias, scale):
 
 
 def decode_group_gated(q, K, V, b, desc_kind, tau, W=None, budget_tokens=0,
-                       sparsity_bp=0, n_local=1, n_min=0, scale=None):
-    """decode_group with the SAS log-gate bias.  Returns (idx [cnt],
+                       sparsity_bp=0, n_local=1, n_min=0, scale=None, n_current=1):
+    """decode_group with the SAS log-gate bias; n_current trailing blocks keep
+    the unit gate (1: the page's single current block).  Returns (idx [cnt],
     o [G, d], lse [G], bias [cnt])."""
     q, pq = _f32(q)
     G, d = q.shape
@@ -270,7 +271,7 @@ def decode_group_gated(q, K, V, b, desc_kind, tau, W=None, budget_tokens=0,
     bias = np.empty(max(NB, 1), np.float64)
     c = lib().orc_decode_group_gated(pq, G, pK, pV, T, d, b, desc_kind, pW,
                                      budget_tokens, sparsity_bp, n_local, n_min,
-                                     scale, tau, idx.ctypes.data_as(_i32p), NB,
+                                     n_current, scale, tau, idx.ctypes.data_as(_i32p), NB,
                                      o.ctypes.data_as(_f64p), lse.ctypes.data_as(_f64p),
                                      bias.ctypes.data_as(_f64p))
     return idx[:c].copy(), o, lse, bias[:c].copy()

@@ -350,20 +350,23 @@ ORC_API int64_t orc_decode_group(const float* q, int G, const float* K,
 /* 8. Log-gate bias of the selected blocks (SAS)                            */
 /* ------------------------------------------------------------------------ */
 
-/* [SAS] "Method": the C candidate (historical) blocks' selector scores s
- * become normalised gates g = softmax(s) over all C candidates; the current
- * block keeps the unit gate g_0 = 1; the logits of a selected block's tokens
- * get log g added inside the softmax.
+/* [SAS] "Method": the context is split into one always-retained current
+ * block B_0, whose gate stays g_0 = 1, and C historical blocks, whose
+ * selector scores s become normalised gates g = softmax(s) over all C of
+ * them; the logits of a selected historical block's tokens get log g added
+ * inside the softmax.
  * READING: g = softmax(tau * s) with tau > 0 (tau = 1 is the page's form;
  * the scores here are the method's block scores, not a trained selector's
- * logits, so their scale is left to the caller); every local block counts
- * as the current block (bias 0).
- * s: [NB] with the candidates 0..NC-1 scored; idx/cnt: a selection as
+ * logits, so their scale is left to the caller).  n_current trailing blocks
+ * keep the unit gate: 1 is the page's B_0 (every other block, a kept local
+ * one included, is historical: it is scored, enters the normaliser and gets
+ * its log-gate), n_current = n_local treats every local block as current.
+ * s: [NB] with blocks 0..NB-n_current-1 scored; idx/cnt: a selection as
  * orc_select returns it; bias: [cnt], log g of each selected block. */
-ORC_API void orc_gate_bias(const double* s, int64_t NB, int n_local, double tau,
+ORC_API void orc_gate_bias(const double* s, int64_t NB, int n_current, double tau,
                            const int32_t* idx, int64_t cnt, double* bias) {
-    int64_t nl = (n_local < NB) ? n_local : NB;
-    int64_t nc = NB - nl;
+    int64_t nu = (n_current < NB) ? n_current : NB;
+    int64_t nc = NB - nu;
     /* log sum_c exp(tau s_c), with the largest term factored out */
     double m = -INFINITY;
     for (int64_t c = 0; c < nc; ++c)
@@ -416,16 +419,19 @@ ORC_API void orc_attend_biased(const float* q, const float* K, const float* V,
 }
 
 /* A whole decode step with the SAS log-gate bias: orc_decode_group's
- * descriptors, scores, count and selection, then the biased attention.
+ * descriptors, scores, count and selection, then the scores of every
+ * historical block (all but the n_current trailing ones, see orc_gate_bias)
+ * and the biased attention.
  * bias (optional, may be NULL): [idx_cap] receives log g of each selected
  * block. */
 ORC_API int64_t orc_decode_group_gated(const float* q, int G, const float* K,
                                        const float* V, int64_t T, int d, int b,
                                        int desc_kind, const float* W,
                                        int64_t budget_tokens, int sparsity_bp,
-                                       int n_local, int n_min, double scale,
-                                       double tau, int32_t* idx, int64_t idx_cap,
-                                       double* o, double* lse, double* bias) {
+                                       int n_local, int n_min, int n_current,
+                                       double scale, double tau, int32_t* idx,
+                                       int64_t idx_cap, double* o, double* lse,
+                                       double* bias) {
     int64_t NB = orc_nblocks(T, b);
     double* s = (double*)malloc(sizeof(double) * (size_t)(NB > 0 ? NB : 1));
     double* o0 = (double*)malloc(sizeof(double) * (size_t)G * d);
@@ -433,8 +439,25 @@ ORC_API int64_t orc_decode_group_gated(const float* q, int G, const float* K,
     int64_t cnt = orc_decode_group(q, G, K, V, T, d, b, desc_kind, W, budget_tokens,
                                    sparsity_bp, n_local, n_min, scale, idx, idx_cap,
                                    o0, l0, s);
+    /* the historical blocks' scores (the candidates' and those of the kept
+     * local blocks before the current ones), same definition as the
+     * selection's */
+    int64_t nu = (n_current < NB) ? n_current : NB;
+    if (desc_kind == 0) {
+        double* mn = (double*)malloc(sizeof(double) * (size_t)((NB > 0 ? NB : 1) * d));
+        double* mx = (double*)malloc(sizeof(double) * (size_t)((NB > 0 ? NB : 1) * d));
+        orc_desc_minmax(K, T, d, b, mn, mx);
+        orc_score_quest(q, G, d, mn, mx, NB - nu, s);
+        free(mn);
+        free(mx);
+    } else {
+        double* mean = (double*)malloc(sizeof(double) * (size_t)((NB > 0 ? NB : 1) * d));
+        orc_desc_mean(K, T, d, b, mean);
+        orc_score_gate(q, G, d, W, mean, NB - nu, s);
+        free(mean);
+    }
     double* g = (double*)malloc(sizeof(double) * (size_t)(cnt > 0 ? cnt : 1));
-    orc_gate_bias(s, NB, n_local, tau, idx, cnt, g);
+    orc_gate_bias(s, NB, (int)nu, tau, idx, cnt, g);
     for (int h = 0; h < G; ++h)
         orc_attend_biased(q + (int64_t)h * d, K, V, T, d, b, idx, cnt, g, scale,
                           o + (int64_t)h * d, lse + h);

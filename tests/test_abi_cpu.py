@@ -182,6 +182,17 @@ def test_gate_tau_rejected_when_bias_requested(tau):
     assert bsa.block_count(P, 100, 64) == 10   # the count ignores the gate
 
 
+@pytest.mark.parametrize("gc", [-1, 3])
+def test_gate_current_rejected_outside_the_local_blocks(gc):
+    # with a bias requested, the current blocks are 0 (= 1) .. n_local of the
+    # local blocks; without one the field is not read
+    P = bsa.SelectParams(sparsity_bp=9000, n_local=2, n_max=10, gate_tau=0.1,
+                         gate_bias=_FakeDev(), gate_current=gc)
+    assert _select(L_ok(), P) == bsa.ERR_PARAM
+    P2 = bsa.SelectParams(sparsity_bp=9000, n_local=2, n_max=10, gate_current=gc)
+    assert _select(L_ok(), P2, ws_bytes=16) == bsa.ERR_WORKSPACE  # validation went past it
+
+
 def test_decode_gated_validation():
     L = L_ok()
     C = bsa.c_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)

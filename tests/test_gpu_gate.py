@@ -1,7 +1,11 @@
 """GPU parity of the log-gate bias ("Simple Attention Sparsification",
-Method: softmax gates over the candidate blocks, log g added to a kept
-block's logits) against the fp64 oracle: the bias the selecting call writes
-next to each kept block id, and the gated decode that consumes it.
+Method: one current block with the unit gate, softmax gates over the
+historical blocks, log g added to a kept block's logits) against the fp64
+oracle: the bias the selecting call writes next to each kept block id, and
+the gated decode that consumes it.  By default only the last block is
+current, so with two local blocks the older one is historical: scored,
+gated and part of the normaliser; the option gate_current = n_local treats
+every local block as current.
 
 Selection bit-exact (inputs carry a score gap at the top-n boundary).
 Bias: the kernel works from fp32 scores; a score error ds moves a bias by at
@@ -21,7 +25,7 @@ from test_gpu_parity import BF16, F32, MEAN, MINMAX, make_inputs
 pytestmark = pytest.mark.gpu
 
 GATE_CASES = [
-    # dtype, d, blk, kind, Hq, Hkv, lengths, budget, bp, n_local, n_min
+    # dtype, d, blk, kind, Hq, Hkv, lengths, budget, bp, n_local, n_min[, gate_current]
     (BF16, 128, 64, MINMAX, 8, 2, [1000, 1537], 256, 0, 1, 0),
     (BF16, 128, 128, MEAN, 8, 2, [3000, 2049], 0, 9000, 2, 0),
     (BF16, 128, 256, MINMAX, 8, 4, [5000, 1], 0, 9500, 1, 4),   # a group with no candidate
@@ -31,10 +35,19 @@ GATE_CASES = [
     # mid-size rows (about 1900 and 3100 candidates)
     (BF16, 64, 32, MINMAX, 4, 1, [60000], 0, 9000, 1, 2),
     (BF16, 64, 32, MINMAX, 8, 2, [98000, 40000], 0, 9500, 2, 4),
+    # three local blocks, two of them historical; and the option that keeps
+    # every local block current
+    (BF16, 128, 64, MINMAX, 8, 2, [4000, 2500], 0, 9000, 3, 2),
+    (BF16, 128, 64, MINMAX, 8, 2, [4000, 2500], 0, 9000, 2, 2, 2),
+    (BF16, 128, 128, MEAN, 8, 2, [3000, 2049], 0, 9000, 3, 0, 3),
+    # every kept block local (nothing picked), the older ones historical
+    (BF16, 64, 64, MINMAX, 4, 2, [300, 250], 0, 9900, 3, 0),
 ]
 
 
-def _oracle_gated(L, P, q, Ks, Vs, lengths, tau, Wg):
+def _oracle_gated(L, P, q, Ks, Vs, lengths, tau, Wg, n_current):
+    """Oracle selection, outputs and biases per group, and the largest
+    |score| over the historical blocks (for the bias bar)."""
     G = L.Hq // L.Hkv
     kind = 0 if L.desc_kind == MINMAX else 1
     scale = 1.0 / math.sqrt(L.d)
@@ -45,14 +58,17 @@ def _oracle_gated(L, P, q, Ks, Vs, lengths, tau, Wg):
             idx, o, lse, b = O.decode_group_gated(qg, K, V, L.block, kind, tau, W=Wg,
                                                   budget_tokens=P.budget_tokens,
                                                   sparsity_bp=P.sparsity_bp,
-                                                  n_local=P.n_local, n_min=P.n_min, scale=scale)
-            _, _, _, sc = O.decode_group(qg, K, V, L.block, kind, W=Wg,
-                                         budget_tokens=P.budget_tokens,
-                                         sparsity_bp=P.sparsity_bp, n_local=P.n_local,
-                                         n_min=P.n_min, scale=scale, want_scores=True)
-            fin = sc[np.isfinite(sc)]
-            if fin.size:
-                smax = max(smax, float(np.abs(fin).max()))
+                                                  n_local=P.n_local, n_min=P.n_min, scale=scale,
+                                                  n_current=n_current)
+            NB = -(-T // L.block)
+            if kind == 0:
+                mn, mx = O.desc_minmax(K, L.block)
+                sh = O.score_quest(qg, mn, mx)
+            else:
+                sh = O.score_gate(qg, Wg, O.desc_mean(K, L.block))
+            sh = sh[:max(0, NB - n_current)]
+            if sh.size:
+                smax = max(smax, float(np.abs(sh).max()))
             ref[(s, h)] = (idx, o, lse)
             bias[(s, h)] = b
     return ref, bias, smax
@@ -74,11 +90,13 @@ def _tau_for(L, P, q, Ks, lengths, Wg):
 @pytest.mark.parametrize("case", GATE_CASES, ids=[f"g{i}" for i in range(len(GATE_CASES))])
 def test_gated_select_decode_parity(case):
     import torch
-    dtype, d, blk, kind, Hq, Hkv, lengths, budget, bp, nl, nm = case
+    dtype, d, blk, kind, Hq, Hkv, lengths, budget, bp, nl, nm = case[:11]
+    n_current = case[11] if len(case) > 11 else 1
     B = len(lengths)
     max_blocks = (max(lengths) + blk - 1) // blk + 2
     L = bsa.Layout(B, Hq, Hkv, d, blk, max_blocks, dtype, kind)
-    P = bsa.SelectParams(budget_tokens=budget, sparsity_bp=bp, n_local=nl, n_min=nm)
+    P = bsa.SelectParams(budget_tokens=budget, sparsity_bp=bp, n_local=nl, n_min=nm,
+                         gate_current=n_current)
     P.n_max = bsa.block_count(P, max_blocks, blk)
     q, Ks, Vs, Wg = make_inputs(31 + len(lengths), B, Hq, Hkv, d, lengths, dtype, kind)
     enforce_gap(L, P, q, Ks, [[T] for T in lengths], W_gate=Wg)
@@ -106,15 +124,15 @@ def test_gated_select_decode_parity(case):
     bsa.sparse_decode_gated(L, cache, q_dev, idx, cnt, P.gate_bias, P.n_max, 1.0 / math.sqrt(d),
                             o, lse, ws)
     torch.cuda.synchronize()
-    ref, rbias, smax = _oracle_gated(L, P, q, Ks, Vs, lengths, tau, Wg)
+    ref, rbias, smax = _oracle_gated(L, P, q, Ks, Vs, lengths, tau, Wg, n_current)
     compare_step(L, idx, cnt, o, lse, ref)
     gb = P.gate_bias.cpu().numpy()
     cn = cnt.cpu().numpy()
     worst = 0.0
     for (s, h), rb in rbias.items():
         c = int(cn[s, h])
-        NC = max(0, -(-lengths[s] // blk) - nl)
-        tol = tau * 2e-5 * smax + 1e-4 + NC * 1.2e-7
+        NH = max(0, -(-lengths[s] // blk) - n_current)  # historical blocks
+        tol = tau * 2e-5 * smax + 1e-4 + NH * 1.2e-7
         err = np.abs(gb[s, h, :c] - rb).max() if c else 0.0
         assert err <= tol, f"group {(s, h)}: bias err {err} > {tol}"
         assert np.all(gb[s, h, c:] == 0.0)
@@ -252,7 +270,7 @@ def test_gated_topn_long_row_of_ties():
     bsa.sparse_decode_gated(L, cache, q_dev, idx, cnt, P.gate_bias, P.n_max, 1.0 / math.sqrt(d),
                             o, lse, ws)
     torch.cuda.synchronize()
-    ref, rbias, smax = _oracle_gated(L, P, q, Ks, Vs, [T], tau, None)
+    ref, rbias, smax = _oracle_gated(L, P, q, Ks, Vs, [T], tau, None, 1)
     compare_step(L, idx, cnt, o, lse, ref)
     assert {7, 1000, 4321, 7777, 7990} <= set(ref[(0, 0)][0].tolist())
     c = int(cnt[0, 0])

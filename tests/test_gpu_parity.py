@@ -581,9 +581,13 @@ def test_resa_decode_loop(gated):
                         tol = 1e-3 * max(1.0, abs(lo_k), mag[kept].max(), mag[dropped].max())
                         assert lo_k >= hi_d - tol, (k, s, h, lo_k, hi_d)
                 if gated:
-                    rb = O.gate_bias(sc[:NC], NB, 2, tau, sel)
-                    smax = float(np.abs(sc[:NC]).max()) if NC > 0 else 0.0
-                    assert np.abs(gb[s, h, :c] - rb).max() <= tau * 2e-5 * smax + 1e-4 + NC * 1.2e-7
+                    # the page's partition: only the last block is current, so
+                    # the older local block is historical (scored and gated)
+                    mn, mx = O.desc_minmax(K, blk)
+                    sh = O.score_quest(qg, mn, mx)[:NB - 1]
+                    rb = O.gate_bias(sh, NB, 1, tau, sel)
+                    smax = float(np.abs(sh).max()) if NB > 1 else 0.0
+                    assert np.abs(gb[s, h, :c] - rb).max() <= tau * 2e-5 * smax + 1e-4 + NB * 1.2e-7
                 for g in range(G):
                     if gated:
                         ro, rl = O.attend_biased(qg[g], K, V, blk, sel, rb, scale)

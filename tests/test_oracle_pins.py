@@ -535,11 +535,37 @@ def test_attend_biased_zero_bias_is_attend():
     assert abs(l1 - l2) < 1e-15
 
 
-@pytest.mark.parametrize("kind", [0, 1])
-def test_decode_group_gated_matches_selection_and_sdpa(kind):
+def test_gate_bias_current_block_only():
+    """The page's partition: only the last block keeps the unit gate; an
+    older local block is historical -- its gate is its own log_softmax entry
+    and its score enters every other gate's normaliser.  Catches the reading
+    that treats every local block as current (bias 0 there, a normaliser
+    without its score)."""
+    from scipy.special import log_softmax
+    r = rng(67)
+    NB, tau = 30, 0.8
+    s = 3 * r.standard_normal(NB - 1)            # every block but the current one
+    s[NB - 2] = s.max() + 1.0                    # a dominant older local block
+    idx = np.array([3, 11, 20, NB - 2, NB - 1], np.int32)
+    g = O.gate_bias(s, NB, 1, tau, idx)
+    ref = log_softmax(tau * s)
+    np.testing.assert_allclose(g[:4], ref[[3, 11, 20, NB - 2]], rtol=0, atol=1e-13)
+    assert g[4] == 0.0
+    # every local block current: block NB-2 unbiased and out of the normaliser
+    g2 = O.gate_bias(s, NB, 2, tau, idx)
+    ref2 = log_softmax(tau * s[:NB - 2])
+    np.testing.assert_allclose(g2[:3], ref2[[3, 11, 20]], rtol=0, atol=1e-13)
+    assert g2[3:].tolist() == [0.0, 0.0]
+    assert np.all(g[:3] < g2[:3] - 0.1)          # the dominant block takes gate mass
+
+
+@pytest.mark.parametrize("kind,n_current", [(0, 1), (1, 1), (0, 2)])
+def test_decode_group_gated_matches_selection_and_sdpa(kind, n_current):
     """The gated step keeps the ungated step's selection, and its outputs are
-    torch SDPA with log_softmax(tau*s) of the candidate scores (0 on the local
-    blocks) as the float mask."""
+    torch SDPA with log_softmax(tau*s) over the historical blocks' scores as
+    the float mask: every block but the n_current trailing ones is historical
+    (0 on the current ones).  The scores of the kept local blocks that are
+    historical come from the pinned descriptor and score functions."""
     from scipy.special import log_softmax
     r = rng(65 + kind)
     T, b, d, G, nl = 1500, 64, 16, 4, 2
@@ -551,11 +577,21 @@ def test_decode_group_gated_matches_selection_and_sdpa(kind):
     idx0, _, _, s = O.decode_group(q, K, V, b, kind, W=W, budget_tokens=6 * 64,
                                    n_local=nl, n_min=2, want_scores=True)
     idx, o, lse, bias = O.decode_group_gated(q, K, V, b, kind, tau, W=W,
-                                             budget_tokens=6 * 64, n_local=nl, n_min=2)
+                                             budget_tokens=6 * 64, n_local=nl, n_min=2,
+                                             n_current=n_current)
     assert idx.tolist() == idx0.tolist()
     NB = (T + b - 1) // b
-    ls = log_softmax(tau * s[:NB - nl])
-    ref_bias = np.array([ls[j] if j < NB - nl else 0.0 for j in idx])
+    nh = NB - n_current                           # historical blocks
+    if kind == 0:
+        mn, mx = O.desc_minmax(K, b)
+        s_all = O.score_quest(q, mn, mx)
+    else:
+        s_all = O.score_gate(q, W, O.desc_mean(K, b))
+    np.testing.assert_array_equal(s_all[:NB - nl], s[:NB - nl])
+    ls = log_softmax(tau * s_all[:nh])
+    ref_bias = np.array([ls[j] if j < nh else 0.0 for j in idx])
+    if n_current < nl:
+        assert ref_bias[-2] != 0.0                # the older local block is gated
     np.testing.assert_allclose(bias, ref_bias, rtol=0, atol=1e-12)
     m = _bias_mask(T, b, idx, ref_bias)
     scale = 1 / math.sqrt(d)
