@@ -127,9 +127,13 @@ def parse():
     ap.add_argument("--gate-tau", type=float, default=None,
                     help="also time the headline workload with the log-gate bias "
                          "(select writes it, bsa_sparse_decode_gated adds it) at this tau")
-    ap.add_argument("--resa-sweep", action="store_true",
-                    help="also run the ragged ReSA loop over f in {16,32,64,128} x p in "
-                         "{0.9,0.95,0.98} and compare its bytes with 1/b + (1-p) + 1/f")
+    ap.add_argument("--no-resa-sweep", action="store_true",
+                    help="skip the ragged ReSA loop over f in {16,32,64,128} x p in "
+                         "{0.9,0.95,0.98} (bytes against 1/b + (1-p) + 1/f)")
+    ap.add_argument("--sweep-steps", type=int, default=0,
+                    help="timed steps per sweep point (0: 2f, two rectifies)")
+    ap.add_argument("--rectify-f", type=int, default=None,
+                    help="rectify interval of a rectifying --workload (default: the workload's)")
     return ap.parse_args()
 
 
@@ -299,6 +303,30 @@ def step_bytes(run, lens):
     return desc, kv
 
 
+def expected_counts(run, lens):
+    """Kept blocks of every sequence at lengths lens by the closed form
+    (bsa_block_count): the count the byte accounting assumes, which every KV
+    head's selection must report."""
+    b = run.w.block
+    return [run.bsa.block_count(run.P, (T + b - 1) // b, b) for T in lens]
+
+
+def check_counts(cnts, expected):
+    """cnts: per layer, the [B, Hkv] kept counts copied back from the device
+    after the timed steps; raises unless every group reports its sequence's
+    expected count.  Returns the number of groups checked."""
+    import numpy as np
+    n = 0
+    for layer, c in enumerate(cnts):
+        c = np.asarray(c)
+        for s, e in enumerate(expected):
+            if not np.all(c[s] == e):
+                raise RuntimeError(f"layer {layer}, sequence {s}: kept counts {c[s].tolist()}, "
+                                   f"the closed form gives {e}")
+            n += c.shape[1]
+    return n
+
+
 def rectify_cost(run, lens):
     """Bytes (full-cache K and V read) and flops of one rectify call, one layer."""
     w = run.w
@@ -369,6 +397,10 @@ def measure(run, steps, warmup, seed=1):
     torch.cuda.synchronize()
     run.steps_done += steps
     graph_ms = e0.elapsed_time(e1)
+    # the selection the timed steps left behind: every layer's counts equal
+    # the closed form the byte accounting uses
+    counts_checked = check_counts([run.cnt[l].cpu().numpy() for l in range(run.layers)],
+                                  expected_counts(run, run.lengths()))
     # (3) the decode call alone: every layer's call on its current selection,
     # captured into a graph and replayed between two events, so the per-call
     # time is the GPU's own (the eager pass above is host-bound for the short
@@ -399,6 +431,7 @@ def measure(run, steps, warmup, seed=1):
         "decode_us_avg": dec_graph_us,
         "decode_us_eager_events": sum(dec_us) / len(dec_us),
         "decode_kv_bytes_per_call": k1 / steps,
+        "counts_checked": counts_checked,
     }
     if rect_us:
         # The eager per-call events above include the host's launch gaps
@@ -432,7 +465,8 @@ def summarize(w, bp, layers, m):
          "eager_us_per_step_layer": round(m["eager"]["us_per_step_layer"], 2),
          "decode_kernel_us": round(m["decode_us_avg"], 2),
          "decode_GBps": round(m["decode_kv_bytes_per_call"] / (m["decode_us_avg"] * 1e-6) / 1e9, 1),
-         "bytes_per_step_layer": int(gm["eff_bytes_per_step_layer"])}
+         "bytes_per_step_layer": int(gm["eff_bytes_per_step_layer"]),
+         "kept_counts_checked": m["counts_checked"]}
     if not w.rectify_f:
         # the step's time outside the decode call: append + scoring + top-n
         sel = gm["us_per_step_layer"] - m["decode_us_avg"]
@@ -519,7 +553,8 @@ def main():
 
     import workloads as W
     dev = torch.device("cuda:0")
-    w = W.get(args.workload)
+    w = W.get(args.workload) if args.rectify_f is None else \
+        W.get(args.workload, rectify_f=args.rectify_f)
     sweep = [args.sparsity_bp] if args.sparsity_bp is not None else \
         ([w.sparsity_bp] + [b for b in w.sparsity_sweep if b != w.sparsity_bp])
     t0 = time.time()
@@ -601,7 +636,7 @@ def main():
             print(f"# {name}: {time.time() - t0:.1f}s {json.dumps(mx)}", file=sys.stderr, flush=True)
             del rx
             torch.cuda.empty_cache()
-    if args.resa_sweep:
+    if not args.no_resa_sweep and not args.headline_only:
         out["resa_sweep"] = resa_sweep(args, dev)
     print(json.dumps(out), flush=True)
 
@@ -618,7 +653,7 @@ def resa_sweep(args, dev):
         for bp in (9000, 9500, 9800):
             w = W.get("resa_ragged", rectify_f=f, sparsity_bp=bp)
             run = Run(w, args.layers, dev)
-            m = measure(run, max(args.steps, 2 * f), args.warmup)
+            m = measure(run, args.sweep_steps or 2 * f, args.warmup)
             gm = m["graph"]
             dense = sum(T * w.Hkv * 2 * w.d * 2 for T in w.T0)
             rows.append({"f": f, "sparsity_bp": bp,

@@ -82,3 +82,28 @@ def test_traffic_is_reported_only_for_the_measured_sources(monkeypatch, tmp_path
     changed.write_text(open(src).read() + "\nint one_more_line;\n")
     monkeypatch.setattr(bench, "TRAFFIC_SOURCES", (str(changed),) + bench.TRAFFIC_SOURCES[1:])
     assert bench.measured_traffic("long_512k", 9000) is None
+
+
+class _FakeRun:
+    """The parts of a benchmark run the count check reads."""
+    def __init__(self, w, bp):
+        import block_sparse_attention_build_amd as bsa
+        self.w, self.bsa = w, bsa
+        self.P = bsa.SelectParams(budget_tokens=w.budget_tokens, sparsity_bp=bp,
+                                  n_local=w.n_local, n_min=w.n_min)
+
+
+def test_kept_counts_are_checked_against_the_closed_form():
+    import numpy as np
+    w = W.get("resa_ragged")
+    run = _FakeRun(w, w.sparsity_bp)
+    lens = [t + 5 for t in w.T0]
+    exp = bench.expected_counts(run, lens)
+    # 16K: n_min = 16 binds; the others ceil(0.05 * NB)
+    assert exp == [16, 39, 77, 103]
+    good = [np.tile(np.array(exp)[:, None], (1, w.Hkv)) for _ in range(3)]
+    assert bench.check_counts(good, exp) == 3 * w.B * w.Hkv
+    bad = [g.copy() for g in good]
+    bad[2][1, 4] += 1
+    with pytest.raises(RuntimeError, match="layer 2, sequence 1"):
+        bench.check_counts(bad, exp)

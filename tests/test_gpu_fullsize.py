@@ -266,3 +266,106 @@ def test_fullsize_resa_rectify_then_decode():
         assert el <= LSE_RTOL, (s, h, el)
     F.append_one()
     select_decode_and_check(F, P, ws)
+
+
+def test_fullsize_resa_loop_two_rectifies():
+    """The ragged ReSA loop at full size for 2f steps: every step appends a
+    token and selects (the fused append + select the benchmark times) and
+    decodes; after steps f and 2f the last f tokens are rectified.  On two
+    sampled groups (the 16K and the 128K sequence) the oracle follows on host
+    copies that take the same rewrites: the rectify rows at each rectify, and
+    the selection (bit-exact), o and lse at sampled steps before, between and
+    after the rectifies.  The candidates' score gap holds at every checked
+    length: over 2f = 64 steps no block changes from local to candidate
+    (contexts start block-aligned), and the rewritten tokens lie in the
+    current block."""
+    torch = _torch()
+    w = W.get("resa_ragged")
+    f = w.rectify_f
+    G = w.G
+    steps = 2 * f
+    sampled = [(0, 1), (3, 6)]
+    F = Filled(w, w.T0, sampled, 1006, extra=steps)
+    P = F.params[w.sparsity_bp]
+    assert all(t % w.block == 0 for t in w.T0) and steps <= w.block
+    F.enforce([P], [t + steps for t in w.T0])
+    F.allocate_and_prefill()
+    ws = F.workspace(f)
+    scale = 1.0 / math.sqrt(w.d)
+    tdt = torch.bfloat16
+    rng = np.random.Generator(np.random.PCG64(78))
+    idx = torch.empty(w.B, w.Hkv, P.n_max, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(w.B, w.Hkv, dtype=torch.int32, device="cuda")
+    o = torch.empty(w.B, w.Hq, w.d, dtype=tdt, device="cuda")
+    lse = torch.empty(w.B, w.Hq, dtype=torch.float32, device="cuda")
+    check_at = {1, 2, f - 1, f, f + 1, f + 17, steps}
+    n_checked = 0
+    for k in range(1, steps + 1):
+        # one decode step: the step's query is fresh, the sampled groups' from host
+        qh = W.quantize(rng.standard_normal((w.B, w.Hq, w.d), dtype=np.float32), w.dtype)
+        for (s, h) in sampled:
+            qh[s, h * G:(h + 1) * G] = F.q[s, h * G:(h + 1) * G]
+        toks = [F.device_tokens(s, T, T + 1) for s, T in enumerate(F.T)]
+        kn = torch.cat([a for a, _ in toks])
+        vn = torch.cat([b for _, b in toks])
+        F.cache.seq_lens += 1
+        F.T = [T + 1 for T in F.T]
+        q_dev = torch.from_numpy(qh).to("cuda", tdt)
+        bsa.append_select(F.L, F.cache, kn, vn, q_dev, P, idx, cnt, ws)
+        bsa.sparse_decode(F.L, F.cache, q_dev, idx, cnt, P.n_max, scale, o, lse, ws)
+        if k in check_at:
+            torch.cuda.synchronize()
+            gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+            go, gl = o.float().cpu().numpy(), lse.cpu().numpy()
+            for (s, h) in sampled:
+                T = F.T[s]
+                ridx, ro, rl = O.decode_group(F.q[s, h * G:(h + 1) * G], F.K[s][h][:T],
+                                              F.V[s][h][:T], w.block, 0,
+                                              sparsity_bp=P.sparsity_bp, n_local=P.n_local,
+                                              n_min=P.n_min, scale=scale)
+                c = int(gc[s, h])
+                assert c == len(ridx) and np.array_equal(gi[s, h, :c], ridx), (k, s, h)
+                assert np.abs(go[s, h * G:(h + 1) * G] - ro).max() <= O_TOL, (k, s, h)
+                el = np.abs(gl[s, h * G:(h + 1) * G] - rl) / np.maximum(1.0, np.abs(rl))
+                assert el.max() <= LSE_RTOL, (k, s, h)
+                n_checked += 1
+        if k % f == 0:
+            # rectify the last f tokens of every sequence
+            qr = W.quantize(rng.standard_normal((w.B, w.Hq, f, w.d), dtype=np.float32), w.dtype)
+            kr = torch.empty(w.B, w.Hkv, f, w.d, dtype=tdt, device="cuda")
+            vr = torch.empty_like(kr)
+            new = {}
+            for s in range(w.B):
+                for h in range(w.Hkv):
+                    if (s, h) in F.sampled:
+                        ks, vs = F.kscale[(s, h)]
+                        Ts = F.T[s]
+                        kh = W.quantize(F.K[s][h][Ts - f:Ts] + 0.1 * ks *
+                                        rng.standard_normal((f, w.d), dtype=np.float32), "bf16")
+                        vh = W.quantize(F.V[s][h][Ts - f:Ts] + 0.1 * vs *
+                                        rng.standard_normal((f, w.d), dtype=np.float32), "bf16")
+                        new[(s, h)] = (kh, vh)
+                        kr[s, h] = torch.from_numpy(kh).to("cuda", tdt)
+                        vr[s, h] = torch.from_numpy(vh).to("cuda", tdt)
+                    else:
+                        kr[s, h] = torch.randn(f, w.d, device="cuda").to(tdt)
+                        vr[s, h] = torch.randn(f, w.d, device="cuda").to(tdt)
+            orr = torch.empty(w.B, w.Hq, f, w.d, dtype=tdt, device="cuda")
+            lr = torch.empty(w.B, w.Hq, f, dtype=torch.float32, device="cuda")
+            bsa.rectify_chunk(F.L, F.cache, torch.from_numpy(qr).to("cuda", tdt), kr, vr, f,
+                              scale, orr, lr, ws)
+            torch.cuda.synchronize()
+            orr, lr = orr.float().cpu().numpy(), lr.cpu().numpy()
+            for (s, h) in sampled:
+                Ts = F.T[s]
+                kh, vh = new[(s, h)]
+                # the oracle rewrites the host copies in place, which the
+                # following steps' checks then see
+                ro, rl = O.rectify(qr[s, h * G:(h + 1) * G], F.K[s][h][:Ts], F.V[s][h][:Ts],
+                                   kh, vh, scale)
+                assert np.array_equal(F.K[s][h][Ts - f:Ts], kh)
+                assert np.abs(orr[s, h * G:(h + 1) * G] - ro).max() <= O_TOL, (k, s, h)
+                el = np.abs(lr[s, h * G:(h + 1) * G] - rl) / np.maximum(1.0, np.abs(rl))
+                assert el.max() <= LSE_RTOL, (k, s, h)
+                n_checked += 1
+    assert n_checked == 2 * (len(check_at) + 2)
