@@ -442,6 +442,7 @@ bsa_status bsa_rectify_chunk(const bsa_layout* layout, const bsa_cache* cache, c
     a.chunk_tiles = w.plan.chunk_tiles;
     a.wgs = w.plan.wgs;
     a.rows_per_wg = w.plan.rows_per_wg;
+    a.sets = w.plan.sets;
     a.scale_log2 = softmax_scale * kLog2e;
     a.o_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.o_part);
     a.lse_part = reinterpret_cast<float*>(static_cast<char*>(ws) + w.lse_part);

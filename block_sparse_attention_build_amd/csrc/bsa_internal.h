@@ -72,6 +72,7 @@ struct RectifyArgs {
     int chunk_tiles;      // fp32: 32-token tiles per chunk
     int wgs;              // bf16: workgroups launched (even shares of all tiles)
     int rows_per_wg;      // bf16: rows of a row group
+    int sets;             // bf16: sets of workgroups (one row group each) in the 256-row shape, else 1
     float scale_log2;
     float* o_part;        // bf16: [slot][rows_per_wg][d]; fp32: [B*Hq*f][S][d]
     float* lse_part;      // bf16: [slot][rows_per_wg];    fp32: [B*Hq*f][S]
@@ -84,7 +85,7 @@ struct RectifyPlan {
     int64_t o_floats;
     int64_t lse_floats;
     int splits, chunk_tiles;  // fp32 path
-    int wgs, rows_per_wg;     // bf16 path
+    int wgs, rows_per_wg, sets;  // bf16 path
 };
 hipError_t launch_rectify(const CacheArgs& c, const RectifyArgs& a, hipStream_t stream);
 void rectify_plan(const CacheArgs& c, int f, RectifyPlan* plan);

@@ -8,27 +8,27 @@
 // run first (kv_write.hip, overwrite mode); this file computes, for query i of
 // head h (position T-f+i), softmax attention over tokens 0..T-f+i.
 //
-// bf16 path: the only dense contraction of the method, on
-// v_mfma_f32_16x16x32_bf16.  Rows = the G*f queries of a GQA group (G*f = 128
-// for G = 4, f = 32), handled in row groups of up to 64 (4 waves), 128 (8
-// waves) or 256 (8 waves of two 16-row tiles) rows.  The tiles of all
-// (sequence, KV head, row group) groups are dealt out in equal contiguous
-// shares to a fixed number of workgroups (two per CU), so ragged lengths
-// cost no load imbalance; each run of a share inside one group yields one
-// partial (o, base-2 lse) per row, merged afterwards in list order.
-// K/V tiles (16 KiB at d = 128) stream through an LDS ring fed by direct
-// global->LDS copies, two (4 stages, two workgroups per CU) or four (6
-// stages, one per CU) tiles ahead of the one being computed, with one
-// workgroup barrier per tile; every wave reads its matrix operands from LDS
-// with conflict-free 16-byte reads.  Per tile and 16-row tile: S^T = K Q^T (2 x d/32 MFMAs), causal
-// mask, online softmax with a lazily moved reference max, O += P V with P in
-// bf16 (d/16 MFMAs).
+// bf16 path: the only dense contraction of the method.  Rows = the G*f
+// queries of a GQA group.  The tiles of all groups are dealt out in equal
+// contiguous shares to a fixed number of workgroups (stream-K), so ragged
+// lengths cost no load imbalance; each run of a share inside one group yields
+// one partial (o, base-2 lse) per row, merged afterwards in list order.  K/V
+// tiles (32 tokens, 16 KiB at d = 128) stream through an LDS ring fed by
+// direct global->LDS copies.  Two shapes:
+//  - up to 128 rows (row groups of 64 with 4 waves or 128 with 8 waves, two
+//    workgroups per CU): one 16-row tile per wave on v_mfma_f32_16x16x32_bf16,
+//    a 4-stage ring two tiles ahead, one workgroup barrier per tile;
+//  - more rows: row groups of 256 on v_mfma_f32_32x32x16_bf16, one workgroup
+//    of 8 waves per CU running a ping-pong schedule (below).
+// Both take the online softmax with a lazily moved reference max and P in
+// bf16.
 //
 // fp32 path: fixed token chunks per workgroup, plain VALU arithmetic, the
 // chunk merge of decode.hip.
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "bsa_device.h"
 #include "bsa_internal.h"
@@ -36,6 +36,8 @@
 namespace bsa {
 
 namespace {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
@@ -51,9 +53,6 @@ constexpr int kWaves = kThreads / kWave;
 constexpr float kRebase = 8.f;  // log2 headroom before the running max is moved
 constexpr int kChunkTiles = BSA_RECTIFY_CHUNK_TILES;  // 32-token tiles per workgroup
 constexpr int kStages = BSA_RECTIFY_STAGES;           // tiles in flight per workgroup (LDS ring)
-#ifndef BSA_RECTIFY_STAGES_WIDE
-#define BSA_RECTIFY_STAGES_WIDE 6  // ring stages of the one-workgroup-per-CU shape
-#endif
 
 struct RectifyParams {
     CacheArgs c;
@@ -436,11 +435,408 @@ void rectify_bf16_kernel(RectifyParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// 256-row shape (more than 128 rows per KV head): one workgroup of 8 waves per
+// CU, two 16-row tiles per wave, an 8-stage LDS ring.
+//
+// Ping-pong schedule.  Waves 0-3 (group A) and 4-7 (group B) share the four
+// SIMDs pairwise and work half a tile apart: in every phase (the span between
+// two workgroup barriers) one wave of each SIMD runs its matrix products
+// while the other reads its next operands from LDS and runs the softmax, so
+// the matrix cores, the VALU and the LDS are busy at the same time instead of
+// in turn.  Per wave and tile k the VALU phase reads K(k+1) and V(k-1) from
+// LDS and takes the softmax of tile k (scores from the previous matrix
+// phase); the matrix phase computes S(k+1) = K(k+1) Q^T and O += P(k-1)
+// V(k-1) (32 MFMAs).  Group A's phases are 2k (VALU) and 2k+1 (matrix);
+// group B's are 2k+1 and 2k+2.  Only group A copies tiles into the ring, NS -
+// 3 ahead, and waits for its copies of tile k+1 before the barrier that opens
+// phase 2k; the last reader of a stage (group B's V read) is done two phases
+// before the stage is refilled.
+//
+// The softmax takes no maximum on its common path: the exponentials use the
+// current reference max, and only when some lane's sum of its eight
+// exponentials exceeds 2^kRebase (or is not finite) does the wave take the
+// slow path, which finds the tile's row maxima (permlane swaps across the four
+// lane groups of a row), moves the reference, rescales O and the row sums and
+// recomputes P.  The reference starts at +inf in exponent units, so the first
+// tile of every piece takes the slow path.
+//
+// More than 256 rows go to further sets of workgroups, one row group each.
+// Every set runs the same stream-K split of the same tile list, so workgroup w
+// of every set reads the same tiles at about the same time; the set size is a
+// multiple of 8, which puts those workgroups on one XCD (workgroups are dealt
+// to the eight XCDs in turn), so the later reads of a tile hit that XCD's L2
+// instead of HBM.  Page ids come from the page table by scalar loads issued
+// one tile before they are used.
+// ---------------------------------------------------------------------------
+constexpr int kWideRows = 256;  // rows per workgroup: 8 waves x two 16-row tiles
+constexpr int kWideStages = 8;  // LDS ring stages (16 KiB each at d = 128)
+constexpr int kWideWGs = 256;   // workgroups resident at once: one per CU
+constexpr float kPmax = 256.f;  // 2^kRebase: largest lane sum of exponentials on the fast path
+
+int wide_sets(int R) { return (R + kWideRows - 1) / kWideRows; }
+int wide_set_wgs(int Z) {
+    const int w = (kWideWGs / Z) / 8 * 8;
+    return w < 8 ? 8 : w;
+}
+// workgroups of a set that take tiles, for N tiles in the list
+__device__ __forceinline__ int wide_wgs(int64_t N, int per_set) {
+    if (N <= 0) return 0;
+    return static_cast<int>(min(static_cast<int64_t>(per_set), (N + kMinTilesPerWG - 1) / kMinTilesPerWG));
+}
+
+// Maximum of v and the value in lane ^ 32, returned to both lanes.
+__device__ __forceinline__ float half_swap_max(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Workgroup barrier that no instruction is scheduled across (the phases of
+// the ping-pong must stay on their side of it) and no LDS access moves across.
+__device__ __forceinline__ void phase_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int D, int BLK>
+__global__ __launch_bounds__(8 * kWave) void rectify_wide_kernel(RectifyParams p) {
+    constexpr int NW = 8;
+    constexpr int NS = kWideStages;
+    constexpr int DIST = NS - 3;
+    constexpr int KQ = D / 16;   // k steps of S^T = K Q^T (16 channels each)
+    constexpr int NB = D / 32;   // 32-channel column blocks of O
+    constexpr int TILE_EL = 32 * D;
+    constexpr int CH = 2 * TILE_EL / 512;  // 1 KiB chunks per tile, K then V
+    constexpr int CPW = CH / (NW / 2);     // chunks each group-A wave copies
+    static_assert(CPW >= 1 && CPW * (NW / 2) == CH, "chunks split evenly over group A");
+    static_assert((NS & (NS - 1)) == 0, "ring stages: a power of two");
+    __shared__ __attribute__((aligned(16))) uint16_t ring[NS][2 * TILE_EL];
+    __shared__ long long s_loc[4];
+
+    const CacheArgs& c = p.c;
+    const RectifyArgs& a = p.a;
+    const int G = c.G;
+    const int f = a.f;
+    const int R = G * f;
+    const int per_set = a.wgs / a.sets;
+    const int z = blockIdx.x / per_set;  // set = row group
+    const int w = blockIdx.x - z * per_set;
+    const int per_seq = c.Hkv;
+    const int64_t slot_base = static_cast<int64_t>(z) * (static_cast<int64_t>(c.B) * c.Hkv + per_set);
+
+    if (threadIdx.x < kWave) {
+        const SeqHit tot = seq_scan(c.seq_lens, c.B, per_seq, -1);
+        const int W = wide_wgs(tot.N, per_set);
+        int64_t x0 = 0, x1 = 0;
+        SeqHit h{tot.N, -1, 0};
+        if (w < W) {
+            x0 = wg_begin(w, tot.N, W);
+            x1 = wg_begin(w + 1, tot.N, W);
+            h = seq_scan(c.seq_lens, c.B, per_seq, x0);
+        }
+        if (threadIdx.x == 0) {
+            s_loc[0] = (w < W && x1 > x0) ? h.s : -1;
+            s_loc[1] = x0 - h.start;
+            s_loc[2] = x1 - x0;
+        }
+    }
+    __syncthreads();
+    int s = __builtin_amdgcn_readfirstlane(static_cast<int>(s_loc[0]));
+    if (s < 0) return;
+    const int64_t pos0 = s_loc[1];
+    const int64_t left0 = s_loc[2];
+    int64_t left = (static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(left0 >> 32))) << 32) |
+                   static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(left0)));
+    int nts = ntiles_of(c.seq_lens[s]);
+    int gl = __builtin_amdgcn_readfirstlane(static_cast<int>(pos0 / nts));
+    int off = __builtin_amdgcn_readfirstlane(static_cast<int>(pos0 - static_cast<int64_t>(gl) * nts));
+
+    const uint16_t* kpool = static_cast<const uint16_t*>(c.k_pool);
+    const uint16_t* vpool = static_cast<const uint16_t*>(c.v_pool);
+    const float sl2 = a.scale_log2;
+
+    while (true) {
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const bool grp_a = wave < NW / 2;
+        const int hf = lane >> 5;  // lane half
+        const int l32 = lane & 31;
+        const int kvh = gl;
+        const int T = c.seq_lens[s];
+        const int t0 = off;
+        const int nt = static_cast<int>(min(left, static_cast<int64_t>(nts - off)));
+        const int64_t slot = slot_base + static_cast<int64_t>(s) * per_seq + gl + w;
+        const int64_t row_base = (static_cast<int64_t>(s) * c.Hq + kvh * G) * f;  // row r = 0
+        const int r_wave = z * kWideRows + wave * 32;                               // first row of this wave
+        const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
+        // page ids by scalar loads (constant address space: the table is
+        // never written by this kernel)
+        const __attribute__((address_space(4))) int32_t* ptrow_s =
+            (const __attribute__((address_space(4))) int32_t*)(ptrow);
+        const int64_t head_off = static_cast<int64_t>(kvh) * (BLK * D) + lane * 8;
+        // per-lane LDS element offsets of the K (A operand) and V (B operand)
+        // pieces inside a ring stage, from the page's operand order
+        const int k_lane = (l32 >> 4) * (D / 32) * 512 + ((lane & 15) + 16 * hf) * 8;
+        const int v_lane = TILE_EL + (l32 >> 4) * 512 + (lane & 15) * 8 + hf * 128;
+
+        __syncthreads();  // the previous piece is done with the ring
+
+        // B operand of S^T = K Q^T: row r_wave + l32, channels 16 kq + 8 hf ..
+        const int r_me = r_wave + l32;
+        const int pos = (r_me < R) ? T - f + (r_me % f) : T - 1;  // query position of the lane's row
+        bf16x8 qb[KQ];
+        {
+            const uint16_t* qp = static_cast<const uint16_t*>(a.q) + (row_base + r_me) * D + 8 * hf;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq) {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (r_me < R) v = ldg16(qp + kq * 16);
+                qb[kq] = __builtin_bit_cast(bf16x8, v);
+            }
+        }
+        floatx16 oacc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) oacc[nb][e] = 0.f;
+        float m_run = -INFINITY, l_run = 0.f;
+        float nms = INFINITY;  // forces the slow path on the first tile
+        wait_vmcnt<0>();
+
+        auto page_of = [&](int t) __attribute__((always_inline)) {
+            return ptrow_s[__builtin_amdgcn_readfirstlane((32 * t) / BLK)];
+        };
+        // group A: queue the copies of tile t (page id pg) into ring stage buf
+        auto issue = [&](int t, int buf, int pg) __attribute__((always_inline)) {
+            const int tok0 = 32 * t;
+            const int64_t goff = static_cast<int64_t>(pg) * c.Hkv * (BLK * D) + head_off + (tok0 % BLK) * D;
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int ch = wave * CPW + i;
+                const uint16_t* src = (ch < CH / 2) ? kpool + goff + ch * 512
+                                                    : vpool + goff + (ch - CH / 2) * 512;
+                copy16_to_lds(src, &ring[buf][ch * 512]);
+            }
+        };
+        auto read_k = [&](u32x4* kr, int buf) __attribute__((always_inline)) {
+            const uint16_t* st = ring[buf] + k_lane;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq)
+                kr[kq] = *reinterpret_cast<const u32x4*>(st + (kq >> 1) * 512 + (kq & 1) * 256);
+        };
+        auto read_v = [&](u32x4* vr, int buf) __attribute__((always_inline)) {
+            const uint16_t* st = ring[buf] + v_lane;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    vr[2 * nb + m] = *reinterpret_cast<const u32x4*>(st + nb * 1024 + m * 256);
+        };
+
+        const int t_last = t0 + nt - 1;
+        int pg_next = 0;
+        if (grp_a) {
+#pragma unroll
+            for (int k = 0; k < DIST; ++k)
+                if (k < nt) issue(t0 + k, k, page_of(t0 + k));
+            pg_next = page_of(min(t0 + DIST, t_last));
+            if (nt >= DIST)
+                wait_vmcnt<CPW * (DIST - 1)>();
+            else
+                wait_vmcnt<0>();
+        }
+        phase_barrier();  // tile 0 is in the ring
+
+        // S^T of tile 0 of the piece (both groups): accumulator element 4j + i
+        // holds token 8j + 4 hf + i of the tile for the lane's row
+        floatx16 sc;
+        u32x4 kr[KQ];
+        u32x4 vr[2 * NB];
+        read_k(kr, 0);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+#pragma unroll
+        for (int kq = 0; kq < KQ; ++kq)
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[kq]), qb[kq], sc, 0, 0, 0);
+        bf16x8 pk[2], pprev[2];  // P of tokens {8m + 4hf + i, 16 + 8m + 4hf + i}: the A operands of PV
+        if (!grp_a) phase_barrier();  // group B runs one phase behind
+
+        // tiles from k_mask on reach into the causal tail [T - f + 1, T)
+        const int k_mask = max(0, min(nt, (T - f + 1) / 32 - t0));
+        // one tile: VALU phase (LDS reads for the next matrix phase, softmax of
+        // tile k), then matrix phase (S(k+1), O += P(k-1) V(k-1))
+        auto iter = [&](int k, auto mask_tag) __attribute__((always_inline)) {
+            constexpr bool masked = decltype(mask_tag)::value;
+            const int t = t0 + k;
+            if (grp_a) {
+                if (k + DIST < nt) {
+                    issue(t + DIST, (k + DIST) & (NS - 1), pg_next);
+                    pg_next = page_of(min(t + DIST + 1, t_last));
+                    wait_vmcnt<CPW * (DIST - 1)>();  // this wave's copies of tile k + 1 have landed
+                } else {
+                    wait_vmcnt<0>();
+                }
+            }
+            phase_barrier();
+            // ---- VALU phase ----
+            read_k(kr, (k + 1) & (NS - 1));
+            if (k > 0) read_v(vr, (k - 1) & (NS - 1));
+            __builtin_amdgcn_sched_barrier(0);  // the reads go out first; the softmax hides their latency
+            const int tok_lane = 32 * t + 4 * hf;
+            float pr[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float x = sc[e];
+                if (masked) x = (tok_lane + 8 * (e >> 2) + (e & 3) <= pos) ? x : -INFINITY;
+                pr[e] = __builtin_amdgcn_exp2f(fmaf(x, sl2, nms));
+            }
+            float ls = (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]))) +
+                       (((pr[8] + pr[9]) + (pr[10] + pr[11])) + ((pr[12] + pr[13]) + (pr[14] + pr[15])));
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pk[m][i] = static_cast<__bf16>(pr[4 * m + i]);
+                    pk[m][4 + i] = static_cast<__bf16>(pr[4 * m + 8 + i]);
+                }
+            float alpha = 1.f;
+            const bool resc = __ballot(!(ls <= kPmax)) != 0;  // uniform
+            if (resc) {
+                // slow path: find the row maxima of the tile, move the reference
+                float x[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    x[e] = sc[e];
+                    if (masked) x[e] = (tok_lane + 8 * (e >> 2) + (e & 3) <= pos) ? x[e] : -INFINITY;
+                }
+                float tmax = x[0];
+#pragma unroll
+                for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, x[e]);
+                tmax = half_swap_max(tmax);  // the row's other 16 tokens sit in lane ^ 32
+                const float m_new = fmaxf(m_run, tmax);
+                const bool none = (m_new == -INFINITY);  // the row has seen no token yet
+                alpha = none ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
+                m_run = m_new;
+                nms = none ? INFINITY : -m_new * sl2;
+                const float nm = none ? 0.f : nms;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(x[e], sl2, nm));
+                ls = (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]))) +
+                     (((pr[8] + pr[9]) + (pr[10] + pr[11])) + ((pr[12] + pr[13]) + (pr[14] + pr[15])));
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pk[m][i] = static_cast<__bf16>(pr[4 * m + i]);
+                        pk[m][4 + i] = static_cast<__bf16>(pr[4 * m + 8 + i]);
+                    }
+            }
+            l_run = l_run * alpha + ls;
+            // ---- matrix phase: S(k+1), O += P(k-1) V(k-1) ----
+            phase_barrier();
+#pragma unroll
+            for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+#pragma unroll
+            for (int kq = 0; kq < KQ; ++kq)
+                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[kq]), qb[kq], sc, 0, 0, 0);
+            if (k > 0) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int m = 0; m < 2; ++m)
+                        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            pprev[m], __builtin_bit_cast(bf16x8, vr[2 * nb + m]), oacc[nb], 0, 0, 0);
+            }
+            if (resc) {
+                // O (tiles up to k - 1, at the old scale) moves to the new
+                // reference: row 8j + 4 hf + i of element 4j + i takes the
+                // alpha of the lane holding that row
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float al = __shfl(alpha, 8 * (e >> 2) + 4 * hf + (e & 3), 64);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) oacc[nb][e] *= al;
+                }
+            }
+            pprev[0] = pk[0];
+            pprev[1] = pk[1];
+        };
+        int k = 0;
+        for (; k < k_mask; ++k) iter(k, std::false_type{});
+        for (; k < nt; ++k) iter(k, std::true_type{});
+        if (grp_a) phase_barrier();  // group A ends one phase earlier
+
+        // PV of the piece's last tile (the only one that can run past T)
+        {
+            read_v(vr, (nt - 1) & (NS - 1));
+            const int nvalid = T - 32 * t_last;
+            if (nvalid < 32) {
+                // zero V of the tokens past T: k-slot e of m holds token
+                // 8m + 4hf + e (e < 4) or 16 + 8m + 4hf + e - 4
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int tok = 8 * m + 4 * hf + (e & 3) + 16 * (e >> 2);
+                        if (tok >= nvalid) {
+                            const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+#pragma unroll
+                            for (int nb = 0; nb < NB; ++nb) vr[2 * nb + m][e >> 1] &= keep;
+                        }
+                    }
+            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        pprev[m], __builtin_bit_cast(bf16x8, vr[2 * nb + m]), oacc[nb], 0, 0, 0);
+        }
+
+        // partials of this wave's rows for the piece, in slot `slot`: element
+        // 4j + i of block nb is row 8j + 4 hf + i, channel 32 nb + l32
+        const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int rr = 8 * (e >> 2) + 4 * hf + (e & 3);
+            const float L = __shfl(l_tot, rr, 64);
+            const float M = __shfl(m_run, rr, 64);
+            const int r = r_wave + rr;
+            if (r >= R) continue;
+            const int64_t prow = slot * kWideRows + (r - z * kWideRows);
+            float* op = a.o_part + prow * D + l32;
+            const bool empty = (M == -INFINITY);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) op[nb * 32] = empty ? 0.f : oacc[nb][e] / L;
+            if (l32 == 0) a.lse_part[prow] = empty ? -INFINITY : M * sl2 + log2f(L);
+        }
+
+        left -= nt;
+        if (left <= 0) break;
+        off = 0;
+        if (++gl == per_seq) {
+            gl = 0;
+            do {
+                ++s;
+                nts = ntiles_of(c.seq_lens[s]);
+            } while (nts == 0);
+        }
+    }
+}
+
 // Merge of the pieces of every row of the bf16 path, in list order.  One
 // workgroup per 16 rows of a row group: 16 threads per row, each owning d/16
 // channels; the row's pieces (one partial per slot, RWG partial rows apart)
-// are read four at a time and weighted by 2^(lse_k - M).
-template <int RWG, int D>
+// are read four at a time and weighted by 2^(lse_k - M).  WIDE: the
+// 256-row shape, whose row groups are sets of workgroups over one list of
+// (sequence, KV head) groups; otherwise the row groups are groups of the
+// list.
+template <int RWG, int D, bool WIDE>
 __global__ __launch_bounds__(256) void rectify_merge_kernel(RectifyParams p) {
     constexpr int CPT = D / 16;  // channels per thread
     static_assert(CPT % 4 == 0, "float4 channel groups");
@@ -449,7 +845,7 @@ __global__ __launch_bounds__(256) void rectify_merge_kernel(RectifyParams p) {
     const RectifyArgs& a = p.a;
     const int R = c.G * a.f;
     const int Z = (R + RWG - 1) / RWG;
-    const int per_seq = c.Hkv * Z;
+    const int per_seq = WIDE ? c.Hkv : c.Hkv * Z;
     const int nrb = (R + 15) / 16;
     const int grp = blockIdx.x / nrb;  // s * Hkv + kvh
     const int r0 = (blockIdx.x - grp * nrb) * 16;
@@ -468,9 +864,12 @@ __global__ __launch_bounds__(256) void rectify_merge_kernel(RectifyParams p) {
     __syncthreads();
     const int64_t N = s_loc[0];
     const int nts = ntiles_of(c.seq_lens[s]);
-    const int W = stream_wgs(N, a.wgs);
-    const int gl = kvh * Z + zg;
+    const int per_set = WIDE ? a.wgs / a.sets : a.wgs;
+    const int W = WIDE ? wide_wgs(N, per_set) : stream_wgs(N, a.wgs);
+    const int gl = WIDE ? kvh : kvh * Z + zg;
     const int64_t start = s_loc[1] + static_cast<int64_t>(gl) * nts;
+    const int64_t slot_base =
+        WIDE ? static_cast<int64_t>(zg) * (static_cast<int64_t>(c.B) * c.Hkv + per_set) : 0;
     int w0 = 0, npieces = 0;
     if (nts > 0) {
         w0 = wg_owner(start, N, W);
@@ -480,7 +879,7 @@ __global__ __launch_bounds__(256) void rectify_merge_kernel(RectifyParams p) {
     const int q = tid & 15;
     const int r = r0 + row;
     const bool valid = r < R;
-    const int64_t prow0 = (static_cast<int64_t>(s) * per_seq + gl + w0) * RWG + (r - zg * RWG);
+    const int64_t prow0 = (slot_base + static_cast<int64_t>(s) * per_seq + gl + w0) * RWG + (r - zg * RWG);
     const float* lp = a.lse_part + prow0;
     float M = -INFINITY;
     if (valid)
@@ -599,28 +998,38 @@ __global__ __launch_bounds__(kThreads) void rectify_f32_kernel(RectifyParams p) 
 }
 
 // Rows (G*f) per workgroup: up to 64 with 4 waves, up to 128 with 8 waves of
-// one 16-row tile each (two workgroups per CU), 256 with 8 waves of two
-// tiles (one workgroup per CU, the cache read once).  More rows take several
-// row groups of 128: once the cache is read more than once anyway, two
-// independent workgroups per CU overlap one's matrix work with the other's
-// softmax better than one workgroup of two tiles per wave does (f = 128 at
-// G = 4: 905 against 1036 us per call on the ragged ReSA caches).
-int rows_per_wg(int R) { return R <= 64 ? 64 : (R <= 128 ? 128 : (R <= 256 ? 256 : 128)); }
+// one 16-row tile each (two workgroups per CU), more in the 256-row shape
+// (one workgroup per CU, row groups of 256 in co-scheduled sets).
+int rows_per_wg(int R) { return R <= 64 ? 64 : (R <= 128 ? 128 : kWideRows); }
 
 template <int D, int BLK, int RTW, int NW>
 hipError_t launch_bf16(const RectifyParams& p, hipStream_t stream) {
     constexpr int RWG = 16 * RTW * NW;
-    if (p.a.rows_per_wg != RWG) return hipErrorInvalidValue;
-    constexpr int NS = (RTW == 2) ? BSA_RECTIFY_STAGES_WIDE : kStages;
-    hipLaunchKernelGGL((rectify_bf16_kernel<D, BLK, RTW, NS, NW>), dim3(p.a.wgs),
+    if (p.a.rows_per_wg != RWG || p.a.sets != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((rectify_bf16_kernel<D, BLK, RTW, kStages, NW>), dim3(p.a.wgs),
                        dim3(NW * kWave), 0, stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int R = p.c.G * p.a.f;
     const int64_t wgs = static_cast<int64_t>(p.c.B) * p.c.Hkv * ((R + 15) / 16);
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((rectify_merge_kernel<RWG, D>), dim3(static_cast<uint32_t>(wgs)), dim3(256),
+    hipLaunchKernelGGL((rectify_merge_kernel<RWG, D, false>), dim3(static_cast<uint32_t>(wgs)), dim3(256),
                        0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D, int BLK>
+hipError_t launch_wide(const RectifyParams& p, hipStream_t stream) {
+    const int R = p.c.G * p.a.f;
+    if (p.a.rows_per_wg != kWideRows || p.a.sets != wide_sets(R) || p.a.wgs % p.a.sets != 0)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((rectify_wide_kernel<D, BLK>), dim3(p.a.wgs), dim3(8 * kWave), 0, stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t wgs = static_cast<int64_t>(p.c.B) * p.c.Hkv * ((R + 15) / 16);
+    if (wgs > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((rectify_merge_kernel<kWideRows, D, true>), dim3(static_cast<uint32_t>(wgs)),
+                       dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -628,8 +1037,8 @@ template <int D, int BLK>
 hipError_t launch_bf16_r(const RectifyParams& p, hipStream_t stream) {
     const int R = p.c.G * p.a.f;
     if (R <= 64) return launch_bf16<D, BLK, 1, 4>(p, stream);
-    if (R <= 128 || R > 256) return launch_bf16<D, BLK, 1, 8>(p, stream);
-    return launch_bf16<D, BLK, 2, 8>(p, stream);
+    if (R <= 128) return launch_bf16<D, BLK, 1, 8>(p, stream);
+    return launch_wide<D, BLK>(p, stream);
 }
 
 template <int D>
@@ -661,12 +1070,23 @@ void rectify_plan(const CacheArgs& c, int f, RectifyPlan* pl) {
     if (c.dtype == kBF16) {
         const int R = c.G * f;
         const int rwg = rows_per_wg(R);
-        const int64_t groups = static_cast<int64_t>(c.B) * c.Hkv * ((R + rwg - 1) / rwg);
-        const int64_t n_max = groups * tiles;
-        const int64_t wgs = std::max<int64_t>(kStreamWGs, (n_max + kMaxTilesPerWG - 1) / kMaxTilesPerWG);
-        pl->wgs = static_cast<int>(std::min<int64_t>(wgs, 0x7fffffff));
         pl->rows_per_wg = rwg;
-        const int64_t slots = groups + wgs;
+        int64_t slots;
+        if (rwg == kWideRows) {
+            // sets of workgroups, each over the list of (sequence, KV head) groups
+            const int Z = wide_sets(R);
+            const int per_set = wide_set_wgs(Z);
+            pl->sets = Z;
+            pl->wgs = Z * per_set;
+            slots = static_cast<int64_t>(Z) * (static_cast<int64_t>(c.B) * c.Hkv + per_set);
+        } else {
+            const int64_t groups = static_cast<int64_t>(c.B) * c.Hkv * ((R + rwg - 1) / rwg);
+            const int64_t n_max = groups * tiles;
+            const int64_t wgs = std::max<int64_t>(kStreamWGs, (n_max + kMaxTilesPerWG - 1) / kMaxTilesPerWG);
+            pl->sets = 1;
+            pl->wgs = static_cast<int>(std::min<int64_t>(wgs, 0x7fffffff));
+            slots = groups + wgs;
+        }
         pl->o_floats = slots * rwg * c.d;
         pl->lse_floats = slots * rwg;
     } else {
