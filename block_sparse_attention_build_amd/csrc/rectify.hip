@@ -72,7 +72,8 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, void* lds) {
     // the low 32 bits of a generic LDS address are the LDS offset
     const uint32_t m0 =
         __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds)));
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src));
+    // (an M0 write needs one wait state before an LDS-DMA load reads it)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src));
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -442,23 +443,26 @@ void rectify_bf16_kernel(RectifyParams p) {
 // Ping-pong schedule.  Waves 0-3 (group A) and 4-7 (group B) share the four
 // SIMDs pairwise and work half a tile apart: in every phase (the span between
 // two workgroup barriers) one wave of each SIMD runs its matrix products
-// while the other reads its next operands from LDS and runs the softmax, so
-// the matrix cores, the VALU and the LDS are busy at the same time instead of
-// in turn.  Per wave and tile k the VALU phase reads K(k+1) and V(k-1) from
-// LDS and takes the softmax of tile k (scores from the previous matrix
-// phase); the matrix phase computes S(k+1) = K(k+1) Q^T and O += P(k-1)
-// V(k-1) (32 MFMAs).  Group A's phases are 2k (VALU) and 2k+1 (matrix);
-// group B's are 2k+1 and 2k+2.  Only group A copies tiles into the ring, NS -
-// 3 ahead, and waits for its copies of tile k+1 before the barrier that opens
-// phase 2k; the last reader of a stage (group B's V read) is done two phases
-// before the stage is refilled.
+// while the other runs the exponentials of its softmax, so the matrix cores
+// and the VALU are busy at the same time instead of in turn.  32x32x16 MFMAs
+// take half the issue slots of 16x16x32 ones for the same work, which leaves
+// the other wave's VALU nearly its full rate.  Per wave and tile k, the VALU
+// phase reads K(k+1) from LDS and takes exp2 of tile k's scores (from the
+// previous matrix phase); the matrix phase computes S(k+1) = K(k+1) Q^T and
+// O += P(k-1) V(k-1) (16 MFMAs), with tile k's row sums and bf16 P and the
+// LDS reads of V(k) placed between them.  Group A's phases are 2k (VALU) and
+// 2k+1 (matrix); group B's are 2k+1 and 2k+2.  Only group A copies tiles into
+// the ring: tile k + NS - 3 in its VALU phase k (where it waits for group B's
+// matrix phase anyway), and it waits for its copies of tile k+1 before the
+// barrier that opens phase 2k; the last use of a stage (group B's PV of the
+// tile it held, phase 2k - 2) ends before the stage is refilled.
 //
 // The softmax takes no maximum on its common path: the exponentials use the
-// current reference max, and only when some lane's sum of its eight
+// current reference max, and only when some lane's sum of its sixteen
 // exponentials exceeds 2^kRebase (or is not finite) does the wave take the
-// slow path, which finds the tile's row maxima (permlane swaps across the four
-// lane groups of a row), moves the reference, rescales O and the row sums and
-// recomputes P.  The reference starts at +inf in exponent units, so the first
+// slow path, which finds the tile's row maxima (a permlane swap with the lane
+// holding the row's other half), moves the reference, rescales O and the row
+// sums and recomputes P.  The reference starts at +inf in exponent units, so the first
 // tile of every piece takes the slow path.
 //
 // More than 256 rows go to further sets of workgroups, one row group each.
@@ -639,12 +643,18 @@ __global__ __launch_bounds__(8 * kWave) void rectify_wide_kernel(RectifyParams p
         };
 
         const int t_last = t0 + nt - 1;
-        int pg_next = 0;
+        // Page id of the next tile to copy: pg_load is the scalar load in
+        // flight, pg_next its value.  Scalar and LDS loads share one wait
+        // counter, so the value is taken over right after the matrix phase
+        // has waited for its LDS operands anyway, never where LDS reads are
+        // still in flight.
+        int pg_load = 0, pg_next = 0;
         if (grp_a) {
 #pragma unroll
             for (int k = 0; k < DIST; ++k)
                 if (k < nt) issue(t0 + k, k, page_of(t0 + k));
             pg_next = page_of(min(t0 + DIST, t_last));
+            pg_load = pg_next;
             if (nt >= DIST)
                 wait_vmcnt<CPW * (DIST - 1)>();
             else
@@ -664,6 +674,21 @@ __global__ __launch_bounds__(8 * kWave) void rectify_wide_kernel(RectifyParams p
         for (int kq = 0; kq < KQ; ++kq)
             sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[kq]), qb[kq], sc, 0, 0, 0);
         bf16x8 pk[2], pprev[2];  // P of tokens {8m + 4hf + i, 16 + 8m + 4hf + i}: the A operands of PV
+        // A reference moved in the VALU phase of tile k applies to O once
+        // PV(k-1) is in it: at the start of the next VALU phase (or before
+        // the last PV).  O's element 4j + i of every block is row 8j + 4hf + i
+        // and takes the factor of the lane holding that row.
+        bool resc_pending = false;
+        float alpha_pending = 1.f;
+        auto rescale_o = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float al = __shfl(alpha_pending, 8 * (e >> 2) + 4 * hf + (e & 3), 64);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) oacc[nb][e] *= al;
+            }
+            resc_pending = false;
+        };
         if (!grp_a) phase_barrier();  // group B runs one phase behind
 
         // tiles from k_mask on reach into the causal tail [T - f + 1, T)
@@ -674,19 +699,22 @@ __global__ __launch_bounds__(8 * kWave) void rectify_wide_kernel(RectifyParams p
             constexpr bool masked = decltype(mask_tag)::value;
             const int t = t0 + k;
             if (grp_a) {
-                if (k + DIST < nt) {
-                    issue(t + DIST, (k + DIST) & (NS - 1), pg_next);
-                    pg_next = page_of(min(t + DIST + 1, t_last));
-                    wait_vmcnt<CPW * (DIST - 1)>();  // this wave's copies of tile k + 1 have landed
-                } else {
+                // this wave's copies of tile k + 1 have landed (tiles up to
+                // k - 1 + DIST are queued)
+                if (k + DIST - 1 < nt)
+                    wait_vmcnt<CPW * (DIST - 2)>();
+                else
                     wait_vmcnt<0>();
-                }
             }
             phase_barrier();
-            // ---- VALU phase ----
+            // ---- VALU phase: K(k+1) from LDS, exponentials of tile k ----
             read_k(kr, (k + 1) & (NS - 1));
-            if (k > 0) read_v(vr, (k - 1) & (NS - 1));
+            if (grp_a && k + DIST < nt) {
+                issue(t + DIST, (k + DIST) & (NS - 1), pg_next);
+                pg_load = page_of(min(t + DIST + 1, t_last));
+            }
             __builtin_amdgcn_sched_barrier(0);  // the reads go out first; the softmax hides their latency
+            if (resc_pending) rescale_o();
             const int tok_lane = 32 * t + 4 * hf;
             float pr[16];
 #pragma unroll
@@ -695,15 +723,10 @@ __global__ __launch_bounds__(8 * kWave) void rectify_wide_kernel(RectifyParams p
                 if (masked) x = (tok_lane + 8 * (e >> 2) + (e & 3) <= pos) ? x : -INFINITY;
                 pr[e] = __builtin_amdgcn_exp2f(fmaf(x, sl2, nms));
             }
+            // the lane's sum of exponentials at most 2^kRebase, so every one
+            // is (NaN and inf fail the test); the sum feeds the row sum too
             float ls = (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]))) +
                        (((pr[8] + pr[9]) + (pr[10] + pr[11])) + ((pr[12] + pr[13]) + (pr[14] + pr[15])));
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pk[m][i] = static_cast<__bf16>(pr[4 * m + i]);
-                    pk[m][4 + i] = static_cast<__bf16>(pr[4 * m + 8 + i]);
-                }
             float alpha = 1.f;
             const bool resc = __ballot(!(ls <= kPmax)) != 0;  // uniform
             if (resc) {
@@ -728,22 +751,26 @@ __global__ __launch_bounds__(8 * kWave) void rectify_wide_kernel(RectifyParams p
                 for (int e = 0; e < 16; ++e) pr[e] = __builtin_amdgcn_exp2f(fmaf(x[e], sl2, nm));
                 ls = (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]))) +
                      (((pr[8] + pr[9]) + (pr[10] + pr[11])) + ((pr[12] + pr[13]) + (pr[14] + pr[15])));
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pk[m][i] = static_cast<__bf16>(pr[4 * m + i]);
-                        pk[m][4 + i] = static_cast<__bf16>(pr[4 * m + 8 + i]);
-                    }
             }
-            l_run = l_run * alpha + ls;
-            // ---- matrix phase: S(k+1), O += P(k-1) V(k-1) ----
+            resc_pending = resc;
+            alpha_pending = alpha;
+            // ---- matrix phase: S(k+1), O += P(k-1) V(k-1); the row sums and
+            // bf16 P of tile k and the V(k) reads fill the gaps ----
             phase_barrier();
 #pragma unroll
             for (int e = 0; e < 16; ++e) sc[e] = 0.f;
 #pragma unroll
             for (int kq = 0; kq < KQ; ++kq)
                 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[kq]), qb[kq], sc, 0, 0, 0);
+            asm volatile("s_mov_b32 %0, %1" : "=s"(pg_next) : "s"(pg_load));
+            l_run = l_run * alpha + ls;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pk[m][i] = static_cast<__bf16>(pr[4 * m + i]);
+                    pk[m][4 + i] = static_cast<__bf16>(pr[4 * m + 8 + i]);
+                }
             if (k > 0) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
@@ -752,16 +779,18 @@ __global__ __launch_bounds__(8 * kWave) void rectify_wide_kernel(RectifyParams p
                         oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             pprev[m], __builtin_bit_cast(bf16x8, vr[2 * nb + m]), oacc[nb], 0, 0, 0);
             }
-            if (resc) {
-                // O (tiles up to k - 1, at the old scale) moves to the new
-                // reference: row 8j + 4 hf + i of element 4j + i takes the
-                // alpha of the lane holding that row
+            read_v(vr, k & (NS - 1));  // V(k) for the next matrix phase
+            // interleave: the S MFMAs with the VALU work, the PV MFMAs with
+            // the V reads that replace their operands
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float al = __shfl(alpha, 8 * (e >> 2) + 4 * hf + (e & 3), 64);
+            for (int i = 0; i < KQ; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            }
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) oacc[nb][e] *= al;
-                }
+            for (int i = 0; i < 2 * NB; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             pprev[0] = pk[0];
             pprev[1] = pk[1];
@@ -770,10 +799,11 @@ __global__ __launch_bounds__(8 * kWave) void rectify_wide_kernel(RectifyParams p
         for (; k < k_mask; ++k) iter(k, std::false_type{});
         for (; k < nt; ++k) iter(k, std::true_type{});
         if (grp_a) phase_barrier();  // group A ends one phase earlier
+        if (resc_pending) rescale_o();
 
-        // PV of the piece's last tile (the only one that can run past T)
+        // PV of the piece's last tile (the only one that can run past T;
+        // its V was read in the last matrix phase)
         {
-            read_v(vr, (nt - 1) & (NS - 1));
             const int nvalid = T - 32 * t_last;
             if (nvalid < 32) {
                 // zero V of the tokens past T: k-slot e of m holds token
