@@ -78,38 +78,46 @@ def measured_traffic(workload, bp):
 
 
 def read_ceiling(dev):
-    """The device's streaming-read rate: the best of a few grid sizes of a
-    plain 16-byte streaming read over 4 GiB (libbsa_probe.so), timed with
-    HIP events on the current stream."""
+    """The device's streaming-read rate: the best over a few grid sizes and
+    three access modes (grid-stride plain loads, grid-stride nontemporal
+    loads, one contiguous share per workgroup with nontemporal loads) of a
+    16-byte streaming read over 4 GiB (libbsa_probe.so), timed with HIP
+    events on the current stream."""
     import ctypes
 
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_build_amd", "libbsa_probe.so"))
-    lib.bsa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
-                                   ctypes.c_void_p]
-    lib.bsa_probe_read.restype = ctypes.c_int
-    nbytes, grids = 4 << 30, (8192, 16384, 32768, 65536)
+    lib.bsa_probe_read_mode.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p]
+    lib.bsa_probe_read_mode.restype = ctypes.c_int
+    nbytes = 4 << 30
+    cases = [(0, g) for g in (8192, 16384, 32768, 65536)] + \
+            [(1, g) for g in (8192, 32768)] + [(2, g) for g in (256, 512, 1024, 2048)]
+    names = {0: "grid-stride plain loads", 1: "grid-stride nontemporal loads",
+             2: "contiguous share per workgroup, nontemporal loads"}
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    sink = torch.empty(max(grids) * 256 * 16, dtype=torch.uint8, device=dev)
+    sink = torch.empty(65536 * 256 * 16, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    best, best_g = 0.0, 0
-    for g in grids:
+    best, best_case, by_mode = 0.0, None, {}
+    for mode, g in cases:
         for _ in range(3):
             e0.record()
-            rc = lib.bsa_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), g, stream.cuda_stream)
+            rc = lib.bsa_probe_read_mode(buf.data_ptr(), nbytes, sink.data_ptr(), g, mode, stream.cuda_stream)
             e1.record()
             torch.cuda.synchronize()
             if rc != 0:
-                raise RuntimeError(f"bsa_probe_read failed ({rc})")
+                raise RuntimeError(f"bsa_probe_read_mode failed ({rc})")
             gbps = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+            by_mode[names[mode]] = max(by_mode.get(names[mode], 0.0), round(gbps, 1))
             if gbps > best:
-                best, best_g = gbps, g
+                best, best_case = gbps, (mode, g)
     del buf, sink
     torch.cuda.empty_cache()
-    return {"GBps": round(best, 1), "workgroups": best_g,
-            "probe": "streaming read of 4 GiB, 16-byte loads, grid-stride, best of 8192-65536 "
-                     "workgroups x 3 (libbsa_probe.so)"}
+    return {"GBps": round(best, 1), "workgroups": best_case[1], "mode": names[best_case[0]],
+            "by_mode_GBps": by_mode,
+            "probe": "streaming read of 4 GiB, 16-byte loads, best of three access modes and "
+                     "several grid sizes x 3 (libbsa_probe.so)"}
 
 
 def parse():

@@ -34,17 +34,62 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
     if (acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u) sink[tid] = acc;
 }
 
+// Nontemporal loads; CONTIG: workgroup b reads [b*share, (b+1)*share) with a
+// block-stride loop instead of the grid-stride walk.
+template <bool CONTIG>
+__global__ __launch_bounds__(kThreads) void read_nt_kernel(const u32x4* __restrict__ p, size_t n16,
+                                                           u32x4* sink) {
+    const size_t tid = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+    size_t begin, end, stride;
+    if (CONTIG) {
+        const size_t share = (n16 + gridDim.x - 1) / gridDim.x;
+        begin = static_cast<size_t>(blockIdx.x) * share;
+        end = begin + share < n16 ? begin + share : n16;
+        begin += threadIdx.x;
+        stride = kThreads;
+    } else {
+        begin = tid;
+        end = n16;
+        stride = static_cast<size_t>(gridDim.x) * kThreads;
+    }
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    size_t i = begin;
+    for (; i + (kUnroll - 1) * stride < end; i += kUnroll * stride) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+    }
+    for (; i < end; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+    if (acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u) sink[tid] = acc;
+}
+
 }  // namespace
 
 // Reads `bytes` (a multiple of 16) from the device buffer `buf` with
-// `workgroups` workgroups of 256 threads on `stream`.  `sink`: device memory
-// of at least workgroups * 256 * 16 bytes (normally left untouched).
-// Returns 0, or -1 for a bad argument, -2 for a failed launch.
+// `workgroups` workgroups of 256 threads on `stream`, in access mode `mode`
+// (0, 1 or 2, above).  `sink`: device memory of at least workgroups * 256 *
+// 16 bytes (normally left untouched).  Returns 0, or -1 for a bad argument,
+// -2 for a failed launch.
+extern "C" __attribute__((visibility("default"))) int bsa_probe_read_mode(const void* buf, size_t bytes,
+                                                                          void* sink, int workgroups,
+                                                                          int mode, hipStream_t stream) {
+    if (!buf || !sink || workgroups < 1 || bytes % 16 != 0 || mode < 0 || mode > 2) return -1;
+    const u32x4* p = static_cast<const u32x4*>(buf);
+    u32x4* k = static_cast<u32x4*>(sink);
+    if (mode == 0)
+        hipLaunchKernelGGL(read_kernel, dim3(workgroups), dim3(kThreads), 0, stream, p, bytes / 16, k);
+    else if (mode == 1)
+        hipLaunchKernelGGL(read_nt_kernel<false>, dim3(workgroups), dim3(kThreads), 0, stream, p, bytes / 16, k);
+    else
+        hipLaunchKernelGGL(read_nt_kernel<true>, dim3(workgroups), dim3(kThreads), 0, stream, p, bytes / 16, k);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// Mode 0 of the above.
 extern "C" __attribute__((visibility("default"))) int bsa_probe_read(const void* buf, size_t bytes,
                                                                      void* sink, int workgroups,
                                                                      hipStream_t stream) {
-    if (!buf || !sink || workgroups < 1 || bytes % 16 != 0) return -1;
-    hipLaunchKernelGGL(read_kernel, dim3(workgroups), dim3(kThreads), 0, stream,
-                       static_cast<const u32x4*>(buf), bytes / 16, static_cast<u32x4*>(sink));
-    return hipGetLastError() == hipSuccess ? 0 : -2;
+    return bsa_probe_read_mode(buf, bytes, sink, workgroups, 0, stream);
 }
