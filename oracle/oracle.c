@@ -259,13 +259,18 @@ ORC_API void orc_dense_attend(const float* q, const float* K, const float* V,
         z[t] = scale * acc;
         if (z[t] > m) m = z[t];
     }
+    /* z is overwritten by the weights exp(z_t - m); every sum below still
+     * runs over t in order, so o and lse are those of the per-channel form
+     * sum_t exp(z_t - m) V[t][i], value for value */
     double l = 0.0;
-    for (int64_t t = 0; t < n_tok; ++t) l += exp(z[t] - m);
-    for (int i = 0; i < d; ++i) {
-        double acc = 0.0;
-        for (int64_t t = 0; t < n_tok; ++t) acc += exp(z[t] - m) * V[t * d + i];
-        o[i] = acc / l;
+    for (int64_t t = 0; t < n_tok; ++t) {
+        z[t] = exp(z[t] - m);
+        l += z[t];
     }
+    for (int i = 0; i < d; ++i) o[i] = 0.0;
+    for (int64_t t = 0; t < n_tok; ++t)
+        for (int i = 0; i < d; ++i) o[i] += z[t] * V[t * d + i];
+    for (int i = 0; i < d; ++i) o[i] /= l;
     *lse = m + log(l);
     free(z);
 }
