@@ -212,13 +212,16 @@ def test_fullsize_512k_sparsity_sweep():
         select_decode_and_check(F, F.params[bp], ws)
 
 
-def test_fullsize_resa_rectify_then_decode():
-    """The ragged ReSA workload: caches at T0 + f tokens, one rectify of the
-    last f tokens (checked on the sampled groups' rows and cache contents),
-    then one decode step over the rectified cache."""
+@pytest.mark.parametrize("f", [32, 64, 128])
+def test_fullsize_resa_rectify_then_decode(f):
+    """The ragged ReSA workload at the rectify intervals the ReSA page
+    recommends (Key points: f = 32 or 64, and 128): caches at T0 + f tokens,
+    one rectify of the last f tokens (checked on the sampled groups' rows and
+    cache contents), then one decode step over the rectified cache.  At G = 4,
+    f = 64 is one 256-row group per KV head and f = 128 two, run as two
+    co-scheduled sets of workgroups over the same tile list."""
     torch = _torch()
-    w = W.get("resa_ragged")
-    f = w.rectify_f
+    w = W.get("resa_ragged", rectify_f=f)
     G = w.G
     sampled = [(0, 1), (3, 6)]
     T = [t + f for t in w.T0]
