@@ -306,3 +306,27 @@ def test_static_scratch_decode_validates_before_any_hip_call():
              None) == bsa.ERR_PARAM
     assert f(ctypes.byref(L_ok(d=96).c()), ctypes.byref(C), fake, fake, fake, 10, 0.1, fake,
              fake, None) == bsa.ERR_UNSUPPORTED
+
+
+def test_read_probe_rejects_bad_arguments_before_any_launch():
+    """The benchmark's read probe (libbsa_probe.so, outside the interface):
+    its two exports load, and arguments it cannot serve return -1 before any
+    HIP call (a null buffer or sink, no workgroups, a size that is not whole
+    16-byte loads, an unknown mode, and for the scattered-chunk mode a size
+    that is not whole 16 KiB chunks)."""
+    path = os.path.join(ROOT, "block_sparse_attention_build_amd", "libbsa_probe.so")
+    P = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    P.bsa_probe_read_mode.argtypes = [vp, sz, vp, i32, i32, vp]
+    P.bsa_probe_read_mode.restype = i32
+    P.bsa_probe_read.argtypes = [vp, sz, vp, i32, vp]
+    P.bsa_probe_read.restype = i32
+    fake = ctypes.c_void_p(0x1000)
+    assert P.bsa_probe_read(None, 1 << 20, fake, 8, None) == -1
+    assert P.bsa_probe_read(fake, 1 << 20, None, 8, None) == -1
+    assert P.bsa_probe_read(fake, 1 << 20, fake, 0, None) == -1
+    assert P.bsa_probe_read(fake, (1 << 20) + 8, fake, 8, None) == -1
+    for mode in (-1, 4):
+        assert P.bsa_probe_read_mode(fake, 1 << 20, fake, 8, mode, None) == -1
+    assert P.bsa_probe_read_mode(fake, (16 << 10) + 16, fake, 8, 3, None) == -1
+    assert P.bsa_probe_read_mode(fake, 0, fake, 8, 3, None) == -1
