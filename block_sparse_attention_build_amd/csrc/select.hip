@@ -129,10 +129,31 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
     const bool max_row = (DESC == kMinMax) && (lp * 16 >= D * Gm::ES);
     const int ch0 = (lp * EPL) % D;
 
-    // 1. descriptor loads first, before anything they do not depend on is
+    // 0. the group's queries (G <= 16 values per thread, known before any
+    //    load), requested ahead of the descriptors: the sums in step 2 then
+    //    wait for these alone, in one round trip, while the descriptors are
+    //    still arriving (a loop over the heads with a load per iteration would
+    //    wait for every descriptor load, then make one trip per head)
+    constexpr int kMaxG = 16;
+    const E* qg = static_cast<const E*>(a.q) + (static_cast<int64_t>(s) * c.Hq + kvh * c.G) * D;
+    // the sequence length, with a vector (buffer) load in the same round
+    // trip: a scalar load here would be placed at its first use, after the
+    // descriptors have arrived, and cost a trip of its own
+    const int T_v = __builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(c.seq_lens + s), 0,
+                                          static_cast<int>(sizeof(int32_t)), kBufferWord3),
+        0, 0, 0);
+    // (every thread issues all kMaxG loads, heads past G at head 0's address:
+    //  no branch and no select waits on a loaded value here)
+    const int qi = tid % D;
+    typename Elem<DT>::T qraw[kMaxG];
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) qraw[h] = qg[(h < c.G ? h : 0) * D + qi];
+
+    // 1. descriptor loads next, before anything they do not depend on is
     //    known: indices are clamped to the descriptor array (max_blocks rows),
     //    results past the candidates are discarded below, so every load of
-    //    the workgroup is in flight while the queries and the length arrive.
+    //    the workgroup is in flight while the length arrives.
     const char* base = static_cast<const char*>(c.desc) +
                        (static_cast<int64_t>(grp) * c.max_blocks) * Gm::BR + lp * 16;
     float x[kScoreIters][EPL];
@@ -164,26 +185,27 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
     //    mean-pool: u_i = sum_h q_hi, then w = W u.
     //    (heads summed in order h = 0..G-1)
     __shared__ float qw[2 * D];
-    const E* qg = static_cast<const E*>(a.q) + (static_cast<int64_t>(s) * c.Hq + kvh * c.G) * D;
     if (DESC == kMinMax) {
         if (tid < 2 * D) {
-            const int i = tid % D;
             const bool upper = tid >= D;
             float acc = 0.f;
-            for (int h = 0; h < c.G; ++h) {
-                const float xq = Elem<DT>::load(qg, h * D + i);
-                acc += upper ? fmaxf(xq, 0.f) : fminf(xq, 0.f);
+#pragma unroll
+            for (int h = 0; h < kMaxG; ++h) {
+                const float xq = Elem<DT>::load(qraw, h);
+                if (h < c.G) acc += upper ? fmaxf(xq, 0.f) : fminf(xq, 0.f);
             }
             qw[tid] = acc;
         }
     } else {
         if (tid < D) {
             float acc = 0.f;
-            for (int h = 0; h < c.G; ++h) acc += Elem<DT>::load(qg, h * D + tid);
+#pragma unroll
+            for (int h = 0; h < kMaxG; ++h)
+                if (h < c.G) acc += Elem<DT>::load(qraw, h);
             qw[tid] = acc;
         }
     }
-    const int T = c.seq_lens[s];
+    const int T = __builtin_amdgcn_readfirstlane(T_v);
     const int NB = (T + c.block - 1) / c.block;
     // scored: the candidates, and with a log-gate bias every historical
     // block (all but the gate_current trailing ones, kept local ones included)
