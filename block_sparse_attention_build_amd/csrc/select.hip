@@ -323,14 +323,34 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int T = c.seq_lens[s];
+    int32_t* out = a.idx + static_cast<int64_t>(grp) * a.n_max;
+    const float* sc = a.scores + static_cast<int64_t>(grp) * p.stride;
+    const int base = tid * KPT;
+
+    // the sequence length with a buffer load (a VGPR until it is needed) and
+    // every score group of the thread, all in one round trip: the score loads
+    // depend on nothing but the row's capacity (a multiple of 4; groups past
+    // it read the row's first group), and nothing waits for a load until all
+    // have been issued (a load followed by its conversion would wait for it
+    // before the next load went out)
+    const int T_v = __builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(c.seq_lens + s), 0,
+                                          static_cast<int>(sizeof(int32_t)), kBufferWord3),
+        0, 0, 0);
+    floatx4 v[KPT >= 4 ? KPT / 4 : 1];
+    if constexpr (KPT >= 4) {
+#pragma unroll
+        for (int r = 0; r < KPT; r += 4) {
+            const int g0 = (base + r + 4 <= p.stride) ? base + r : 0;
+            v[r / 4] = *reinterpret_cast<const floatx4*>(sc + g0);
+        }
+    }
+    const int T = __builtin_amdgcn_readfirstlane(T_v);
     const int NB = (T + c.block - 1) / c.block;
     const int nl = min(a.n_local, NB);
     const int NC = NB - nl;
     const int n = block_count(NB, c.block, a.budget_tokens, a.sparsity_bp, a.n_local, a.n_min);
     const int K = n - nl;  // candidates to pick
-    int32_t* out = a.idx + static_cast<int64_t>(grp) * a.n_max;
-    const float* sc = a.scores + static_cast<int64_t>(grp) * p.stride;
 
     // Slots past the candidates hold the key 0, below every real key (the
     // scores are never NaN, so the smallest real key, that of -inf, is
@@ -340,27 +360,23 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     // A wave whose first slot is past the candidates holds only the key 0
     // (KPT is sized for the capacity, the row for the current length): such
     // a wave skips every per-key loop below but takes part in every barrier.
-    const int base = tid * KPT;
     const bool live = wave * kWave * KPT < NC;  // wave-uniform
     uint32_t key[KPT];
 #pragma unroll
     for (int r = 0; r < KPT; ++r) key[r] = 0u;
-    if (live) {
-        if (KPT >= 4) {
-            // branch-free 16-byte loads: the row is padded to a multiple of 4
-            // and groups past the end read the row's first group
+    if constexpr (KPT >= 4) {
+        // the groups loaded above; slots past the candidates get the key 0
+        if (live) {
 #pragma unroll
-            for (int r = 0; r < KPT; r += 4) {
-                const int g0 = (base + r < NC) ? base + r : 0;
-                const floatx4 v = *reinterpret_cast<const floatx4*>(sc + g0);
+            for (int r = 0; r < KPT; r += 4)
 #pragma unroll
-                for (int k = 0; k < 4; ++k) key[r + k] = (base + r + k < NC) ? float_key(v[k]) : 0u;
-            }
-        } else {
-#pragma unroll
-            for (int r = 0; r < KPT; ++r)
-                key[r] = (base + r < NC) ? float_key(sc[base + r]) : 0u;
+                for (int k = 0; k < 4; ++k)
+                    key[r + k] = (base + r + k < NC) ? float_key(v[r / 4][k]) : 0u;
         }
+    } else if (live) {
+#pragma unroll
+        for (int r = 0; r < KPT; ++r)
+            key[r] = (base + r < NC) ? float_key(sc[base + r]) : 0u;
     }
 
     // mode: 0 = pick none, 1 = pick every candidate, 2 = threshold select
