@@ -338,12 +338,16 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
                                           static_cast<int>(sizeof(int32_t)), kBufferWord3),
         0, 0, 0);
     floatx4 v[KPT >= 4 ? KPT / 4 : 1];
+    float v1[KPT >= 4 ? 1 : KPT];
     if constexpr (KPT >= 4) {
 #pragma unroll
         for (int r = 0; r < KPT; r += 4) {
             const int g0 = (base + r + 4 <= p.stride) ? base + r : 0;
             v[r / 4] = *reinterpret_cast<const floatx4*>(sc + g0);
         }
+    } else {
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) v1[r] = sc[(base + r < p.stride) ? base + r : 0];
     }
     const int T = __builtin_amdgcn_readfirstlane(T_v);
     const int NB = (T + c.block - 1) / c.block;
@@ -376,7 +380,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     } else if (live) {
 #pragma unroll
         for (int r = 0; r < KPT; ++r)
-            key[r] = (base + r < NC) ? float_key(sc[base + r]) : 0u;
+            key[r] = (base + r < NC) ? float_key(v1[r]) : 0u;
     }
 
     // mode: 0 = pick none, 1 = pick every candidate, 2 = threshold select
