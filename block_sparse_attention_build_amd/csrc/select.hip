@@ -61,6 +61,17 @@ constexpr int kAliveCap = 2048;  // keys gathered after the first radix pass
 // descriptor's byte count
 constexpr int kBufferWord3 = 0x00020000;
 
+// One int read with a vector (buffer) load, left in a VGPR until the caller
+// takes it with readfirstlane at its use: the load joins the round trip of
+// the vector loads issued with it, where a scalar load would be placed at
+// its first use and waited for on its own.
+__device__ __forceinline__ int load_int_vgpr(const int32_t* p) {
+    return __builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p), 0,
+                                          static_cast<int>(sizeof(int32_t)), kBufferWord3),
+        0, 0, 0);
+}
+
 struct ScoreParams {
     CacheArgs c;
     SelectArgs s;
@@ -136,13 +147,9 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
     //    wait for every descriptor load, then make one trip per head)
     constexpr int kMaxG = 16;
     const E* qg = static_cast<const E*>(a.q) + (static_cast<int64_t>(s) * c.Hq + kvh * c.G) * D;
-    // the sequence length, with a vector (buffer) load in the same round
-    // trip: a scalar load here would be placed at its first use, after the
-    // descriptors have arrived, and cost a trip of its own
-    const int T_v = __builtin_amdgcn_raw_buffer_load_b32(
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(c.seq_lens + s), 0,
-                                          static_cast<int>(sizeof(int32_t)), kBufferWord3),
-        0, 0, 0);
+    // the sequence length, in the same round trip (a scalar load would be
+    // placed after the descriptors have arrived and cost a trip of its own)
+    const int T_v = load_int_vgpr(c.seq_lens + s);
     // (every thread issues all kMaxG loads, heads past G at head 0's address:
     //  no branch and no select waits on a loaded value here)
     const int qi = tid % D;
@@ -333,10 +340,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
     // it read the row's first group), and nothing waits for a load until all
     // have been issued (a load followed by its conversion would wait for it
     // before the next load went out)
-    const int T_v = __builtin_amdgcn_raw_buffer_load_b32(
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(c.seq_lens + s), 0,
-                                          static_cast<int>(sizeof(int32_t)), kBufferWord3),
-        0, 0, 0);
+    const int T_v = load_int_vgpr(c.seq_lens + s);
     floatx4 v[KPT >= 4 ? KPT / 4 : 1];
     float v1[KPT >= 4 ? 1 : KPT];
     if constexpr (KPT >= 4) {
