@@ -138,6 +138,21 @@ class Filled:
 SCORE_RTOL = 1e-4
 
 
+def read_tokens(F, s, h, t0, t1):
+    """K, V [t1 - t0, d] float32 of tokens [t0, t1) of group (s, h) as the
+    device cache holds them, gathered through the page table."""
+    L, b, d = F.L, F.w.block, F.w.d
+    j0, j1 = t0 // b, -(-t1 // b)
+    pages = F.cache.page_table[s, j0:j1].long()
+    km, vm = page_index_maps(L)
+    kp = F.cache.k_pool[pages, h].float().cpu().numpy()
+    vp = F.cache.v_pool[pages, h].float().cpu().numpy()
+    n = (j1 - j0) * b
+    K = np.ascontiguousarray(kp[:, km].reshape(n, d)[t0 - j0 * b:t1 - j0 * b])
+    V = np.ascontiguousarray(vp[:, vm].reshape(n, d)[t0 - j0 * b:t1 - j0 * b])
+    return K, V
+
+
 def group_from_cache(F, s, h):
     """K, V [T_s, d] float32 of group (s, h) as the device cache holds them
     (gathered through the page table), the oracle scores of its full blocks
@@ -146,16 +161,8 @@ def group_from_cache(F, s, h):
     hit = F.readback.get((s, h, T))
     if hit is not None:
         return hit
-    torch = _torch()
-    L, b, d, G = F.L, F.w.block, F.w.d, F.w.G
-    NB = -(-T // b)
-    pages = F.cache.page_table[s, :NB].long()
-    km, vm = page_index_maps(L)
-    kp = F.cache.k_pool[pages, h].float().cpu().numpy()
-    vp = F.cache.v_pool[pages, h].float().cpu().numpy()
-    K = np.ascontiguousarray(kp[:, km].reshape(NB * b, d)[:T])
-    V = np.ascontiguousarray(vp[:, vm].reshape(NB * b, d)[:T])
-    del kp, vp
+    b, d, G = F.w.block, F.w.d, F.w.G
+    K, V = read_tokens(F, s, h, 0, T)
     qg = F.q[s, h * G:(h + 1) * G]
     qa = np.abs(qg.astype(np.float64)).sum(0)
     nfull = T // b
@@ -361,8 +368,14 @@ def test_fullsize_resa_rectify_then_decode(f):
         el = (np.abs(lse[s, h * G:(h + 1) * G] - rl) / np.maximum(1.0, np.abs(rl))).max()
         assert eo <= O_TOL, (s, h, eo)
         assert el <= LSE_RTOL, (s, h, el)
+    # every group's cache now holds its re-encoded tokens, bit for bit
+    kr_all, vr_all = kr.float().cpu().numpy(), vr.float().cpu().numpy()
+    for s in range(w.B):
+        for h in range(w.Hkv):
+            Kc, Vc = read_tokens(F, s, h, T[s] - f, T[s])
+            assert np.array_equal(Kc, kr_all[s, h]) and np.array_equal(Vc, vr_all[s, h]), (s, h)
     F.append_one()
-    select_decode_and_check(F, P, ws)
+    select_decode_and_check(F, P, ws, every_group=True)
 
 
 def test_fullsize_resa_loop_two_rectifies():
