@@ -119,8 +119,9 @@ struct ScoreGeom {
     static constexpr int BPW = BPL * (kScoreThreads / kWave) * kScoreIters;  // blocks per WG
 };
 
-// Scores of the candidate blocks [bx * BPW, (bx + 1) * BPW) of group grp.
-template <int DT, int DESC, int D>
+// Scores of the candidate blocks [bx * BPW, (bx + 1) * BPW) of group grp,
+// for groups of at most MG query heads.
+template <int DT, int DESC, int D, int MG>
 __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int grp) {
     typedef typename Elem<DT>::T E;
     typedef ScoreGeom<DT, DESC, D> Gm;
@@ -145,13 +146,15 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
     //    wait for these alone, in one round trip, while the descriptors are
     //    still arriving (a loop over the heads with a load per iteration would
     //    wait for every descriptor load, then make one trip per head)
-    constexpr int kMaxG = 16;
+    constexpr int kMaxG = MG;
     const E* qg = static_cast<const E*>(a.q) + (static_cast<int64_t>(s) * c.Hq + kvh * c.G) * D;
     // the sequence length, in the same round trip (a scalar load would be
     // placed after the descriptors have arrived and cost a trip of its own)
     const int T_v = load_int_vgpr(c.seq_lens + s);
-    // (every thread issues all kMaxG loads, heads past G at head 0's address:
-    //  no branch and no select waits on a loaded value here)
+    // (every thread issues all MG loads, heads past G at head 0's address:
+    //  no branch and no select waits on a loaded value here; groups of up to
+    //  4 heads have an instance of their own, with 4 loads per thread
+    //  instead of 16)
     const int qi = tid % D;
     typename Elem<DT>::T qraw[kMaxG];
 #pragma unroll
@@ -280,9 +283,9 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
     }
 }
 
-template <int DT, int DESC, int D>
+template <int DT, int DESC, int D, int MG>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
-    score_block<DT, DESC, D>(p, static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y));
+    score_block<DT, DESC, D, MG>(p, static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y));
 }
 
 // Append of one token per sequence fused with the scoring: workgroups
@@ -290,12 +293,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
 // descriptor of its block.  The two roles touch disjoint data -- the token
 // lands in the last block, which is local and never scored -- so they can
 // share one launch.
-template <int DT, int DESC, int D>
+template <int DT, int DESC, int D, int MG>
 __global__ __launch_bounds__(kScoreThreads) void append_score_kernel(ScoreParams sp, KvWriteParams kp,
                                                                      int score_gx) {
     const int bx = static_cast<int>(blockIdx.x);
     if (bx < score_gx)
-        score_block<DT, DESC, D>(sp, bx, static_cast<int>(blockIdx.y));
+        score_block<DT, DESC, D, MG>(sp, bx, static_cast<int>(blockIdx.y));
     else
         kv_write_block<DT, DESC, kScoreThreads>(kp, bx - score_gx, static_cast<int>(blockIdx.y));
 }
@@ -742,7 +745,10 @@ template <int DT, int DESC, int D>
 hipError_t launch_score(const ScoreParams& p, hipStream_t stream) {
     constexpr int BPW = ScoreGeom<DT, DESC, D>::BPW;
     dim3 grid((p.c.max_blocks + BPW - 1) / BPW, p.c.B * p.c.Hkv);
-    hipLaunchKernelGGL((score_kernel<DT, DESC, D>), grid, dim3(kScoreThreads), 0, stream, p);
+    if (p.c.G <= 4)
+        hipLaunchKernelGGL((score_kernel<DT, DESC, D, 4>), grid, dim3(kScoreThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((score_kernel<DT, DESC, D, 16>), grid, dim3(kScoreThreads), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -757,8 +763,12 @@ hipError_t launch_append_score(const ScoreParams& sp, const KvWriteParams& kp, h
     const int score_gx = (sp.c.max_blocks + BPW - 1) / BPW;
     // one token per sequence touches one block
     dim3 grid(score_gx + 1, sp.c.B * sp.c.Hkv);
-    hipLaunchKernelGGL((append_score_kernel<DT, DESC, D>), grid, dim3(kScoreThreads), 0, stream, sp, kp,
-                       score_gx);
+    if (sp.c.G <= 4)
+        hipLaunchKernelGGL((append_score_kernel<DT, DESC, D, 4>), grid, dim3(kScoreThreads), 0, stream,
+                           sp, kp, score_gx);
+    else
+        hipLaunchKernelGGL((append_score_kernel<DT, DESC, D, 16>), grid, dim3(kScoreThreads), 0, stream,
+                           sp, kp, score_gx);
     return hipGetLastError();
 }
 
