@@ -84,22 +84,26 @@ struct Chunk;
 template <>
 struct Chunk<kBF16> {
     static constexpr int N = 8;
-    static __device__ __forceinline__ void load(const void* p, float* out) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+    static __device__ __forceinline__ void unpack(const u32x4 w, float* out) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             out[2 * k] = __uint_as_float(w[k] << 16);
             out[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
         }
     }
+    static __device__ __forceinline__ void load(const void* p, float* out) {
+        unpack(*reinterpret_cast<const u32x4*>(p), out);
+    }
 };
 template <>
 struct Chunk<kF32> {
     static constexpr int N = 4;
-    static __device__ __forceinline__ void load(const void* p, float* out) {
-        const floatx4 w = *reinterpret_cast<const floatx4*>(p);
+    static __device__ __forceinline__ void unpack(const u32x4 w, float* out) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) out[k] = w[k];
+        for (int k = 0; k < 4; ++k) out[k] = __uint_as_float(w[k]);
+    }
+    static __device__ __forceinline__ void load(const void* p, float* out) {
+        unpack(*reinterpret_cast<const u32x4*>(p), out);
     }
 };
 
@@ -119,9 +123,25 @@ struct ScoreGeom {
     static constexpr int BPW = BPL * (kScoreThreads / kWave) * kScoreIters;  // blocks per WG
 };
 
-// Scores of the candidate blocks [bx * BPW, (bx + 1) * BPW) of group grp,
-// for groups of at most MG query heads.
-template <int DT, int DESC, int D, int MG>
+// How a scoring workgroup forms the group's query weights (step 0 and 2
+// below): per-thread loads of up to 16 or up to 4 heads summed into LDS
+// behind a barrier, or (min/max, up to 4 heads) per-lane loads of the
+// lane's own channels with no LDS and no barrier.  The per-lane form does
+// 8x the VALU work, which a launch that fills the chip hides behind its
+// descriptor stream (a 512K-token select of 8 groups, 1032 workgroups:
+// 15.85 -> 15.56 us per call) and a small one does not (a 32K-token one,
+// 72 workgroups: 8.17 -> 8.29 us).
+constexpr int kQ16 = 0, kQ4 = 1, kQLane = 2;
+constexpr int kQLaneMinWorkgroups = 256;
+
+template <int DESC>
+int score_qv(int G, int workgroups) {
+    if (G > 4) return kQ16;
+    return (DESC == kMinMax && workgroups >= kQLaneMinWorkgroups) ? kQLane : kQ4;
+}
+
+// Scores of the candidate blocks [bx * BPW, (bx + 1) * BPW) of group grp.
+template <int DT, int DESC, int D, int QV>
 __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int grp) {
     typedef typename Elem<DT>::T E;
     typedef ScoreGeom<DT, DESC, D> Gm;
@@ -145,20 +165,32 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
     //    load), requested ahead of the descriptors: the sums in step 2 then
     //    wait for these alone, in one round trip, while the descriptors are
     //    still arriving (a loop over the heads with a load per iteration would
-    //    wait for every descriptor load, then make one trip per head)
-    constexpr int kMaxG = MG;
+    //    wait for every descriptor load, then make one trip per head).
+    //    Min/max with up to 4 heads: each lane instead reads, per head, the
+    //    16 bytes of the channels it scores and forms its own weights, so
+    //    the weights need no LDS and no workgroup barrier.
+    constexpr int kMaxG = (QV == kQ16) ? 16 : 4;
+    constexpr bool kLaneW = QV == kQLane;
+    static_assert(!kLaneW || DESC == kMinMax, "per-lane weights are min/max only");
     const E* qg = static_cast<const E*>(a.q) + (static_cast<int64_t>(s) * c.Hq + kvh * c.G) * D;
     // the sequence length, in the same round trip (a scalar load would be
     // placed after the descriptors have arrived and cost a trip of its own)
     const int T_v = load_int_vgpr(c.seq_lens + s);
-    // (every thread issues all MG loads, heads past G at head 0's address:
+    // (every thread issues all kMaxG loads, heads past G at head 0's address:
     //  no branch and no select waits on a loaded value here; groups of up to
-    //  4 heads have an instance of their own, with 4 loads per thread
-    //  instead of 16)
+    //  4 heads have instances of their own, with 4 loads per thread instead
+    //  of 16)
     const int qi = tid % D;
-    typename Elem<DT>::T qraw[kMaxG];
+    typename Elem<DT>::T qraw[kLaneW ? 1 : kMaxG];
+    u32x4 qc[kLaneW ? kMaxG : 1];
+    if constexpr (kLaneW) {
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) qraw[h] = qg[(h < c.G ? h : 0) * D + qi];
+        for (int h = 0; h < kMaxG; ++h)
+            qc[h] = *reinterpret_cast<const u32x4*>(qg + (h < c.G ? h : 0) * D + ch0);
+    } else {
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) qraw[h] = qg[(h < c.G ? h : 0) * D + qi];
+    }
 
     // 1. descriptor loads next, before anything they do not depend on is
     //    known: indices are clamped to the descriptor array (max_blocks rows),
@@ -189,13 +221,20 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
             wl[k] = *reinterpret_cast<const u32x4*>(wg + r * D);
         }
     }
+    // Every load above is issued before anything waits for one: without
+    // this fence (the LDS path's barrier is one too) the compiler moves the
+    // length's early exit ahead of the loads and sinks each query load into
+    // the test of its head, making one round trip per load.
+    asm volatile("" ::: "memory");
     // 2. the group's query weights, once per workgroup, into LDS:
     //    min/max: Q-_i = sum_h min(q_hi, 0) (pairs with the min row) and
     //             Q+_i = sum_h max(q_hi, 0) (pairs with the max row);
     //    mean-pool: u_i = sum_h q_hi, then w = W u.
     //    (heads summed in order h = 0..G-1)
     __shared__ float qw[2 * D];
-    if (DESC == kMinMax) {
+    if constexpr (kLaneW) {
+        // formed per lane below
+    } else if (DESC == kMinMax) {
         if (tid < 2 * D) {
             const bool upper = tid >= D;
             float acc = 0.f;
@@ -220,10 +259,23 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
     // scored: the candidates, and with a log-gate bias every historical
     // block (all but the gate_current trailing ones, kept local ones included)
     const int NC = NB - min(a.gate_bias ? a.gate_current : a.n_local, NB);
-    __syncthreads();
+    if constexpr (!kLaneW) __syncthreads();
     if (c0 >= NC) return;  // uniform across the workgroup
     float wv[EPL];
-    if (DESC == kMinMax) {
+    if constexpr (kLaneW) {
+        // the same sums as the LDS path forms, head by head from 0
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) wv[e] = 0.f;
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+            float qv[EPL];
+            Chunk<DE>::unpack(qc[h], qv);
+            if (h < c.G) {
+#pragma unroll
+                for (int e = 0; e < EPL; ++e) wv[e] += max_row ? fmaxf(qv[e], 0.f) : fminf(qv[e], 0.f);
+            }
+        }
+    } else if (DESC == kMinMax) {
         const float* src = qw + (max_row ? D : 0) + ch0;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) wv[e] = src[e];
@@ -283,9 +335,9 @@ __device__ __forceinline__ void score_block(const ScoreParams& p, int bx, int gr
     }
 }
 
-template <int DT, int DESC, int D, int MG>
+template <int DT, int DESC, int D, int QV>
 __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
-    score_block<DT, DESC, D, MG>(p, static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y));
+    score_block<DT, DESC, D, QV>(p, static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y));
 }
 
 // Append of one token per sequence fused with the scoring: workgroups
@@ -293,12 +345,12 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(ScoreParams p) {
 // descriptor of its block.  The two roles touch disjoint data -- the token
 // lands in the last block, which is local and never scored -- so they can
 // share one launch.
-template <int DT, int DESC, int D, int MG>
+template <int DT, int DESC, int D, int QV>
 __global__ __launch_bounds__(kScoreThreads) void append_score_kernel(ScoreParams sp, KvWriteParams kp,
                                                                      int score_gx) {
     const int bx = static_cast<int>(blockIdx.x);
     if (bx < score_gx)
-        score_block<DT, DESC, D, MG>(sp, bx, static_cast<int>(blockIdx.y));
+        score_block<DT, DESC, D, QV>(sp, bx, static_cast<int>(blockIdx.y));
     else
         kv_write_block<DT, DESC, kScoreThreads>(kp, bx - score_gx, static_cast<int>(blockIdx.y));
 }
@@ -745,10 +797,20 @@ template <int DT, int DESC, int D>
 hipError_t launch_score(const ScoreParams& p, hipStream_t stream) {
     constexpr int BPW = ScoreGeom<DT, DESC, D>::BPW;
     dim3 grid((p.c.max_blocks + BPW - 1) / BPW, p.c.B * p.c.Hkv);
-    if (p.c.G <= 4)
-        hipLaunchKernelGGL((score_kernel<DT, DESC, D, 4>), grid, dim3(kScoreThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((score_kernel<DT, DESC, D, 16>), grid, dim3(kScoreThreads), 0, stream, p);
+    switch (score_qv<DESC>(p.c.G, static_cast<int>(grid.x * grid.y))) {
+        case kQLane:
+            if constexpr (DESC == kMinMax) {
+                hipLaunchKernelGGL((score_kernel<DT, DESC, D, kQLane>), grid, dim3(kScoreThreads), 0,
+                                   stream, p);
+                break;
+            }
+            [[fallthrough]];
+        case kQ4:
+            hipLaunchKernelGGL((score_kernel<DT, DESC, D, kQ4>), grid, dim3(kScoreThreads), 0, stream, p);
+            break;
+        default:
+            hipLaunchKernelGGL((score_kernel<DT, DESC, D, kQ16>), grid, dim3(kScoreThreads), 0, stream, p);
+    }
     return hipGetLastError();
 }
 
@@ -763,12 +825,22 @@ hipError_t launch_append_score(const ScoreParams& sp, const KvWriteParams& kp, h
     const int score_gx = (sp.c.max_blocks + BPW - 1) / BPW;
     // one token per sequence touches one block
     dim3 grid(score_gx + 1, sp.c.B * sp.c.Hkv);
-    if (sp.c.G <= 4)
-        hipLaunchKernelGGL((append_score_kernel<DT, DESC, D, 4>), grid, dim3(kScoreThreads), 0, stream,
-                           sp, kp, score_gx);
-    else
-        hipLaunchKernelGGL((append_score_kernel<DT, DESC, D, 16>), grid, dim3(kScoreThreads), 0, stream,
-                           sp, kp, score_gx);
+    switch (score_qv<DESC>(sp.c.G, static_cast<int>(grid.x * grid.y))) {
+        case kQLane:
+            if constexpr (DESC == kMinMax) {
+                hipLaunchKernelGGL((append_score_kernel<DT, DESC, D, kQLane>), grid, dim3(kScoreThreads),
+                                   0, stream, sp, kp, score_gx);
+                break;
+            }
+            [[fallthrough]];
+        case kQ4:
+            hipLaunchKernelGGL((append_score_kernel<DT, DESC, D, kQ4>), grid, dim3(kScoreThreads), 0,
+                               stream, sp, kp, score_gx);
+            break;
+        default:
+            hipLaunchKernelGGL((append_score_kernel<DT, DESC, D, kQ16>), grid, dim3(kScoreThreads), 0,
+                               stream, sp, kp, score_gx);
+    }
     return hipGetLastError();
 }
 

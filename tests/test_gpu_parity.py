@@ -161,6 +161,10 @@ CASES = [
     (F32, 64, 64, MINMAX, 7, 1, [1500], 0, 8500, 1, 2),
     # 33 x 8 = 264 groups: one split per group, so the merge kernel sees S = 1
     (BF16, 64, 64, MINMAX, 16, 8, [100 + 97 * i for i in range(33)], 512, 0, 1, 2),
+    # fp32 min/max scoring launches of 316 and 280 workgroups (at least 256:
+    # each lane forms its own query weights)
+    (F32, 128, 32, MINMAX, 8, 2, [80000, 3000], 0, 9000, 2, 4),
+    (F32, 64, 32, MINMAX, 16, 4, [70000, 5000], 1024, 0, 1, 2),
 ]
 
 
