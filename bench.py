@@ -4,14 +4,18 @@ One step = the decode hot path for one generated token of every sequence,
 run for L distinct layer caches (default 8, so that the kept-block working
 set cannot stay resident in the 256 MB last-level cache):
   seq_lens += 1                          (shared by the layers)
-  per layer: bsa_append_select     (append the new k, v and update the
+  per layer: bsa_append_select_decode, which is
+             bsa_append_select     (append the new k, v and update the
                                    descriptors = bsa_build_block_desc, then
                                    score every non-local block and keep the
                                    top-n = bsa_select_blocks; the append rides
                                    in the scoring launch)
-             bsa_sparse_decode     (split-K attention over the kept blocks,
-                                    log-sum-exp merge)
+             + bsa_sparse_decode   (split-K attention over the kept blocks,
+                                    log-sum-exp merge) in one call; for rows
+                                    of at most 1024 blocks the top-n runs in
+                                    the decode launch
              bsa_rectify_chunk     (every f steps, workloads with rectification)
+  (--step-form separate times the two calls instead).
 Queries, appended tokens and re-encoded keys/values are fresh per step and
 seeded; caches are generated on the device from the workload recipe.
 
@@ -188,6 +192,9 @@ def parse():
                          "{0.9,0.95,0.98} (bytes against 1/b + (1-p) + 1/f)")
     ap.add_argument("--sweep-steps", type=int, default=0,
                     help="timed steps per sweep point (0: 2f, two rectifies)")
+    ap.add_argument("--step-form", choices=["one_call", "separate"], default="one_call",
+                    help="the timed step as one bsa_append_select_decode call per layer, or as "
+                         "bsa_append_select + bsa_sparse_decode")
     ap.add_argument("--rectify-f", type=int, default=None,
                     help="rectify interval of a rectifying --workload (default: the workload's)")
     return ap.parse_args()
@@ -262,7 +269,7 @@ class Run:
                 del K, V
             self.caches.append(c)
         torch.cuda.synchronize()
-        ws_bytes = max([bsa.workspace_size(self.L, bsa.OP_SELECT, P.n_max) for P in self.params.values()] +
+        ws_bytes = max([bsa.workspace_size(self.L, bsa.OP_STEP, P.n_max) for P in self.params.values()] +
                        [bsa.workspace_size(self.L, bsa.OP_DECODE, P.n_max) for P in self.params.values()])
         self.f = w.rectify_f
         if self.f:
@@ -274,6 +281,7 @@ class Run:
         self.o = [torch.empty(w.B, w.Hq, w.d, dtype=self.tdt, device=dev) for _ in range(layers)]
         self.lse = [torch.empty(w.B, w.Hq, dtype=torch.float32, device=dev) for _ in range(layers)]
         self.gate_tau = None  # set to a float to run the gated step
+        self.one_call = True  # timed steps: bsa_append_select_decode (False: the two calls)
         self.gbias = [torch.zeros(w.B, w.Hkv, n_max_all, dtype=torch.float32, device=dev)
                       for _ in range(layers)]
         if self.f:
@@ -314,13 +322,20 @@ class Run:
             gated = self.gate_tau is not None
             P.gate_tau = self.gate_tau if gated else 0.0
             P.gate_bias = self.gbias[l] if gated else None
-            bsa.append_select(self.L, c, inp["kn"][i, l], inp["vn"][i, l], inp["q"][i, l], P,
-                              self.idx[l], self.cnt[l], self.ws[l])
-            if ev is not None:
-                ev[l][0].record()
-            self.decode_call(l, inp["q"][i, l])
-            if ev is not None:
-                ev[l][1].record()
+            if self.one_call and ev is None:
+                # the whole step in one call (the eager pass below keeps the
+                # two calls, so that events can bracket the decode call)
+                bsa.append_select_decode(self.L, c, inp["kn"][i, l], inp["vn"][i, l],
+                                         inp["q"][i, l], P, self.idx[l], self.cnt[l], self.scale,
+                                         self.o[l], self.lse[l], self.ws[l])
+            else:
+                bsa.append_select(self.L, c, inp["kn"][i, l], inp["vn"][i, l], inp["q"][i, l], P,
+                                  self.idx[l], self.cnt[l], self.ws[l])
+                if ev is not None:
+                    ev[l][0].record()
+                self.decode_call(l, inp["q"][i, l])
+                if ev is not None:
+                    ev[l][1].record()
             if rect:
                 r = i // self.f
                 if ev_r is not None:
@@ -524,7 +539,8 @@ def summarize(w, bp, layers, m):
          "bytes_per_step_layer": int(gm["eff_bytes_per_step_layer"]),
          "kept_counts_checked": m["counts_checked"]}
     if not w.rectify_f:
-        # the step's time outside the decode call: append + scoring + top-n
+        # the step's time beyond the decode call alone: append, scoring and
+        # top-n (in the one-call step, whatever the in-launch selection adds)
         sel = gm["us_per_step_layer"] - m["decode_us_avg"]
         s["select_us"] = round(sel, 2)
         s["select_share"] = round(sel / gm["us_per_step_layer"], 3)
@@ -615,6 +631,7 @@ def main():
         ([w.sparsity_bp] + [b for b in w.sparsity_sweep if b != w.sparsity_bp])
     t0 = time.time()
     run = Run(w, args.layers, dev, keep_host_layer0=not args.no_cpu_baseline, sparsities=sweep)
+    run.one_call = args.step_form == "one_call"
     print(f"# {w.name}: setup {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     results = []
     for bp in sweep:
@@ -646,6 +663,7 @@ def main():
                    "budget_tokens": w.budget_tokens, "n_local": w.n_local, "n_min": w.n_min,
                    "descriptor": "minmax" if w.desc_kind == 0 else "meanpool+gate",
                    "layers": args.layers, "timing": "HIP graph replay of K steps",
+                   "step_form": args.step_form,
                    "parallelism": "none (1 GPU)"},
         "bytes": {"effective_per_step_layer": head["bytes_per_step_layer"],
                   "descriptor_per_step_layer": int(m0["graph"]["desc_bytes"]),
@@ -690,6 +708,7 @@ def main():
             wx = W.get(name)
             t0 = time.time()
             rx = Run(wx, args.layers, dev)
+            rx.one_call = args.step_form == "one_call"
             mx = measure(rx, args.steps if not wx.rectify_f else max(args.steps, 2 * wx.rectify_f),
                          args.warmup)
             out["workloads"].append(summarize(wx, rx.P.sparsity_bp, args.layers, mx)[1])

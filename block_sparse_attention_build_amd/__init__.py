@@ -24,10 +24,10 @@ _LIBPATH = LIB_CHECKED if os.environ.get("BSA_CHECKED") == "1" else LIB_DEFAULT
  ERR_CONTRACT) = range(8)
 DTYPE_F32, DTYPE_BF16 = 0, 1
 DESC_MINMAX, DESC_MEANPOOL = 0, 1
-OP_SELECT, OP_DECODE, OP_RECTIFY = 1, 2, 3
+OP_SELECT, OP_DECODE, OP_RECTIFY, OP_STEP = 1, 2, 3, 4
 
 EXPORTS = ("bsa_build_block_desc", "bsa_select_blocks", "bsa_append_select",
-           "bsa_sparse_decode", "bsa_sparse_decode_gated", "bsa_sparse_decode_static",
+           "bsa_append_select_decode", "bsa_sparse_decode", "bsa_sparse_decode_gated", "bsa_sparse_decode_static",
            "bsa_rectify_chunk", "bsa_workspace_size", "bsa_block_count", "bsa_status_string")
 # bytes of the library's per-GPU scratch array (bsa_sparse_decode_static)
 STATIC_SCRATCH_BYTES = 16 << 20
@@ -75,6 +75,8 @@ def lib():
     L.bsa_build_block_desc.argtypes = [pl, pc, vp, vp, i32, vp, vp]
     L.bsa_select_blocks.argtypes = [pl, pc, vp, pp, vp, vp, vp, sz, vp]
     L.bsa_append_select.argtypes = [pl, pc, vp, vp, vp, pp, vp, vp, vp, sz, vp]
+    L.bsa_append_select_decode.argtypes = [pl, pc, vp, vp, vp, pp, vp, vp, ctypes.c_float, vp,
+                                           vp, vp, sz, vp]
     L.bsa_sparse_decode.argtypes = [pl, pc, vp, vp, vp, i32, ctypes.c_float, vp, vp, vp, sz, vp]
     L.bsa_sparse_decode_gated.argtypes = [pl, pc, vp, vp, vp, vp, i32, ctypes.c_float, vp, vp,
                                           vp, sz, vp]
@@ -87,7 +89,7 @@ def lib():
     L.bsa_status_string.argtypes = [ctypes.c_int]
     L.bsa_status_string.restype = ctypes.c_char_p
     for fn in (L.bsa_build_block_desc, L.bsa_select_blocks, L.bsa_append_select,
-               L.bsa_sparse_decode, L.bsa_sparse_decode_gated, L.bsa_sparse_decode_static,
+               L.bsa_append_select_decode, L.bsa_sparse_decode, L.bsa_sparse_decode_gated, L.bsa_sparse_decode_static,
                L.bsa_rectify_chunk):
         fn.restype = ctypes.c_int
     _lib = L
@@ -323,6 +325,26 @@ def append_select(layout: Layout, cache: Cache, k_new, v_new, q, params: SelectP
                                  _ptr(cnt), _ptr(ws), ws.numel() * ws.element_size(),
                                  _stream(stream))
     _check(st, "bsa_append_select")
+
+
+def append_select_decode(layout: Layout, cache: Cache, k_new, v_new, q, params: SelectParams,
+                         idx, cnt, softmax_scale: float, o, lse, ws, stream=None):
+    """One decode step: append_select then sparse_decode (sparse_decode_gated
+    when params.gate_bias is set), with the same results; ws holds at least
+    workspace_size(layout, OP_STEP, params.n_max) bytes."""
+    import torch
+    L = layout
+    _need_select(L, cache, q, params, idx, cnt, ws)
+    for t, name in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, name, L.torch_dtype(), L.B * L.Hkv * L.d)
+    _need(o, "o", L.torch_dtype(), L.B * L.Hq * L.d)
+    _need(lse, "lse", torch.float32, L.B * L.Hq)
+    st = lib().bsa_append_select_decode(ctypes.byref(L.c()), ctypes.byref(cache.c()), _ptr(k_new),
+                                        _ptr(v_new), _ptr(q), ctypes.byref(params.c()), _ptr(idx),
+                                        _ptr(cnt), float(softmax_scale), _ptr(o), _ptr(lse),
+                                        _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream))
+    _check(st, "bsa_append_select_decode")
 
 
 def sparse_decode(layout: Layout, cache: Cache, q, idx, cnt, n_max: int, softmax_scale: float,

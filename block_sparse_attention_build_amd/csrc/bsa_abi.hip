@@ -302,6 +302,7 @@ size_t bsa_workspace_size(const bsa_layout* layout, int32_t op, int32_t n_max_or
         case BSA_OP_SELECT: return select_ws(c);
         case BSA_OP_DECODE: return decode_ws(c, n_max_or_f).total;
         case BSA_OP_RECTIFY: return rectify_ws(c, n_max_or_f).total;
+        case BSA_OP_STEP: return select_ws(c) + decode_ws(c, n_max_or_f).total;
         default: return 0;
     }
 }
@@ -383,6 +384,71 @@ bsa_status bsa_append_select(const bsa_layout* layout, const bsa_cache* cache, c
     s.gate_bias = params->gate_bias;
     s.gate_current = params->gate_current > 1 ? params->gate_current : 1;
     return hip_status(launch_append_select(c, k_new, v_new, s, stream));
+}
+
+bsa_status bsa_append_select_decode(const bsa_layout* layout, const bsa_cache* cache,
+                                    const void* k_new, const void* v_new, const void* q,
+                                    const bsa_select_params* params, int32_t* idx, int32_t* cnt,
+                                    float softmax_scale, void* o, float* lse, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+    bsa_status st = check_layout(layout);
+    if (st != BSA_OK) return st;
+    if ((st = check_cache(cache)) != BSA_OK) return st;
+    if (!k_new || !v_new || !q || !idx || !cnt || !o || !lse || !ws) return BSA_ERR_NULL;
+    if ((st = check_select_params(layout, params)) != BSA_OK) return st;
+    if (params->n_max > layout->max_blocks) return BSA_ERR_PARAM;
+    if (!scale_ok(softmax_scale)) return BSA_ERR_PARAM;
+    const CacheArgs c = make_args(layout, cache);
+    if (topn_keys_per_thread(c.max_blocks) == 0) return BSA_ERR_UNSUPPORTED;
+    const size_t sel_bytes = select_ws(c);
+    const DecodeWs w = decode_ws(c, params->n_max);
+    if (ws_bytes < sel_bytes + w.total) return BSA_ERR_WORKSPACE;
+    if ((st = contract_cache(c, 1, stream)) != BSA_OK) return st;
+    SelectArgs s;
+    s.q = q;
+    s.gate_w = params->gate_w;
+    s.budget_tokens = params->budget_tokens;
+    s.sparsity_bp = params->sparsity_bp;
+    s.n_local = params->n_local;
+    s.n_min = params->n_min;
+    s.n_max = params->n_max;
+    s.idx = idx;
+    s.cnt = cnt;
+    s.scores = static_cast<float*>(ws);
+    s.gate_tau = params->gate_tau;
+    s.gate_bias = params->gate_bias;
+    s.gate_current = params->gate_current > 1 ? params->gate_current : 1;
+    char* dws = static_cast<char*>(ws) + sel_bytes;
+    DecodeArgs a;
+    a.q = q;
+    a.idx = idx;
+    a.cnt = cnt;
+    a.n_max = params->n_max;
+    a.splits = w.splits;
+    a.scale_log2 = softmax_scale * kLog2e;
+    a.bias = params->gate_bias;
+    a.o_part = reinterpret_cast<float*>(dws + w.o_part);
+    a.lse_part = reinterpret_cast<float*>(dws + w.lse_part);
+    a.o = o;
+    a.lse = lse;
+    const bool in_wg = c.dtype == kBF16 && !params->gate_bias && c.max_blocks <= kDecodeSelectSlots;
+    if (!in_wg) {
+        if ((st = hip_status(launch_append_select(c, k_new, v_new, s, stream))) != BSA_OK)
+            return st;
+        if ((st = contract_kept(c, idx, cnt, a.bias, a.n_max, stream)) != BSA_OK) return st;
+        return hip_status(launch_decode(c, a, stream));
+    }
+    if ((st = hip_status(launch_append_score_only(c, k_new, v_new, s, stream))) != BSA_OK)
+        return st;
+    a.scores = s.scores;
+    a.score_stride = score_stride(c.max_blocks);
+    a.budget_tokens = params->budget_tokens;
+    a.sparsity_bp = params->sparsity_bp;
+    a.n_local = params->n_local;
+    a.n_min = params->n_min;
+    a.idx_out = idx;
+    a.cnt_out = cnt;
+    return hip_status(launch_decode(c, a, stream));
 }
 
 bsa_status bsa_sparse_decode(const bsa_layout* layout, const bsa_cache* cache, const void* q,

@@ -178,6 +178,51 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data
+// format, no swizzle): accesses through it are range-checked against the
+// descriptor's byte count
+constexpr int kBufferWord3 = 0x00020000;
+
+// One int read with a vector (buffer) load, left in a VGPR until the caller
+// takes it with readfirstlane at its use: the load joins the round trip of
+// the vector loads issued with it, where a scalar load would be placed at
+// its first use and waited for on its own.
+__device__ __forceinline__ int load_int_vgpr(const int32_t* p) {
+    return __builtin_amdgcn_raw_buffer_load_b32(
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p), 0,
+                                          static_cast<int>(sizeof(int32_t)), kBufferWord3),
+        0, 0, 0);
+}
+
+// One digit step of an MSB-first radix select, by one wave (every lane gets
+// the answer): h is a 256-bin histogram of the alive keys' current digit;
+// returns the digit that holds the krem-th largest alive key and how many
+// alive keys lie in higher digits.  Lane L covers digits 255-4L .. 252-4L
+// (descending); the counts are suffix sums.
+__device__ __forceinline__ void find_digit256(const int* h, int krem, int lane, int& digit,
+                                              int& above) {
+    int c4[4], hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) hv[i] = h[255 - 4 * lane - i];
+    c4[0] = hv[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) c4[i] = c4[i - 1] + hv[i];
+    const int incl = wave_incl_scan(c4[3]);
+    const int excl = incl - c4[3];
+    int found_i = -1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int ge = excl + c4[i];  // keys whose digit >= this one
+        if (ge >= krem && ge - hv[i] < krem) found_i = i;
+    }
+    const uint64_t bal = __ballot(found_i >= 0);
+    const int src = __ffsll(static_cast<unsigned long long>(bal)) - 1;  // exactly one lane
+    const int my_digit = 255 - 4 * lane - (found_i < 0 ? 0 : found_i);
+    const int my_above = excl + (found_i <= 0 ? 0 : c4[found_i - 1]);
+    digit = __builtin_amdgcn_readlane(my_digit, src);
+    above = __builtin_amdgcn_readlane(my_above, src);
+}
+
 // Order-preserving map of fp32 to uint32 (larger float -> larger key);
 // -0.0 is folded onto +0.0 first.  Inputs are not NaN.
 __device__ __forceinline__ uint32_t float_key(float f) {

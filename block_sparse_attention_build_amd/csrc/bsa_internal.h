@@ -42,6 +42,10 @@ hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t st
 // the append sharing the scoring launch.
 hipError_t launch_append_select(const CacheArgs& c, const void* k_new, const void* v_new,
                                 const SelectArgs& s, hipStream_t stream);
+// The append and the scores of launch_append_select without the top-n
+// launch (the decode kernel then selects in-workgroup: DecodeArgs.scores).
+hipError_t launch_append_score_only(const CacheArgs& c, const void* k_new, const void* v_new,
+                                    const SelectArgs& s, hipStream_t stream);
 // keys-per-thread bucket of the top-n kernel for a given max_blocks (0 = too many)
 int topn_keys_per_thread(int max_blocks);
 // row stride (floats) of the score workspace: max_blocks rounded up to 4
@@ -59,9 +63,21 @@ struct DecodeArgs {
     float* lse_part;   // [B*Hq][S]  (base-2 log-sum-exp of the scaled logits)
     void* o;
     float* lse;
+    // In-workgroup selection (bf16, max_blocks <= kDecodeSelectSlots, no
+    // bias): with scores set, every decode workgroup selects its group's
+    // kept blocks from the score row itself, idx/cnt above are ignored, and
+    // the first split of each group writes the kept list to idx_out/cnt_out.
+    const float* scores = nullptr;  // [B*Hkv][score_stride]
+    int score_stride = 0;
+    int budget_tokens = 0, sparsity_bp = 0, n_local = 1, n_min = 0;
+    int32_t* idx_out = nullptr;     // [B*Hkv][n_max]
+    int32_t* cnt_out = nullptr;     // [B*Hkv]
 };
 hipError_t launch_decode(const CacheArgs& c, const DecodeArgs& a, hipStream_t stream);
 int decode_splits(const CacheArgs& c, int n_max);
+// Blocks per sequence up to which the decode kernel can select in-workgroup
+// (two per thread).
+constexpr int kDecodeSelectSlots = 1024;
 
 struct RectifyArgs {
     const void* q;      // [B][Hq][f][d]

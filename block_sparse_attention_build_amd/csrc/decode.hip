@@ -112,6 +112,128 @@ __device__ __forceinline__ void merge_waves_and_store(const float* sm, const flo
     }
 }
 
+// In-workgroup selection, for rows of at most kDecodeSelectSlots blocks
+// (thread t holds blocks 2t and 2t + 1).  The rule is the top-n kernel's
+// ("Rectified Sparse Attention ...", Key points: dynamic top-n with local
+// blocks and a minimum count; "Simple Attention Sparsification", Method:
+// discrete Top-K with the current block always kept): n = block_count(NB),
+// the nl = min(n_local, NB) last blocks, and the n - nl candidates of largest
+// score (ties to the lower index), found by an MSB-first radix select over
+// order-preserving uint32 keys.  The kept ids and their page ids go to
+// kept/kept_page (LDS, ascending); returns n.  scratch: LDS,
+// kSelScratchInts ints, free again on return.  Ends with a barrier.
+constexpr int kDecWaves = kDecThreads / kWave;
+constexpr int kSelScratchInts = kDecWaves * 256 + 256 + 3 * kDecWaves;
+static_assert(2 * kDecThreads == kDecodeSelectSlots, "two blocks per thread");
+
+__device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block, float sc0,
+                                           float sc1, int pg0, int pg1, int* scratch, int* kept,
+                                           int* kept_page) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    int* hist = scratch;                  // [kDecWaves][256] digit counts, one per wave
+    int* hsum = hist + kDecWaves * 256;   // [256] their sum
+    int* red = hsum + 256;                // [3][kDecWaves] min, max, scan totals
+    const int NB = (T + block - 1) / block;
+    const int nl = min(a.n_local, NB);
+    const int NC = NB - nl;
+    const int n = block_count(NB, block, a.budget_tokens, a.sparsity_bp, a.n_local, a.n_min);
+    const int K = n - nl;  // candidates to pick (0 <= K <= NC)
+    const int c0 = 2 * tid;
+    // slots that are not candidates hold the key 0, below every real key
+    const uint32_t key0 = (c0 < NC) ? float_key(sc0) : 0u;
+    const uint32_t key1 = (c0 + 1 < NC) ? float_key(sc1) : 0u;
+    // keys > tau are taken, and the first need_eq keys == tau (by index):
+    // K = 0 takes nothing (no key exceeds 0xffffffff), K = NC every candidate
+    uint32_t tau = (K == 0) ? 0xffffffffu : 0u;
+    int need_eq = 0;
+    if (K > 0 && K < NC) {  // uniform
+        uint32_t lmin = min(key0 - 1u, key1 - 1u);  // the key 0 wraps to the top
+        uint32_t lmax = max(key0, key1);
+        lmin = wave_min_u32(lmin);
+        lmax = wave_max_u32(lmax);
+        if (lane == 0) {
+            red[wave] = static_cast<int>(lmin);
+            red[kDecWaves + wave] = static_cast<int>(lmax);
+        }
+        __syncthreads();
+        uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) {
+            kmin = min(kmin, static_cast<uint32_t>(red[w]));
+            kmax = max(kmax, static_cast<uint32_t>(red[kDecWaves + w]));
+        }
+        kmin += 1u;
+        const uint32_t range = kmax - kmin;
+        uint32_t prefix = 0;  // of key - kmin, above the current digit
+        int krem = K;         // keys still to take at or below the prefix
+        int shift = (range == 0u) ? 0 : 32 - __clz(static_cast<int>(range));
+        const uint32_t kr0 = key0 - kmin, kr1 = key1 - kmin;
+        while (shift > 0) {  // uniform
+            const int dbits = min(8, shift);
+            shift -= dbits;
+            const int hi = shift + dbits;
+            const uint32_t dmask = (1u << dbits) - 1u;
+            int* hw = hist + wave * 256;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) hw[lane + 64 * i] = 0;  // nobody reads it now
+            if (key0 != 0u && (hi >= 32 || (kr0 >> hi) == (prefix >> hi)))
+                atomicAdd(&hw[(kr0 >> shift) & dmask], 1);
+            if (key1 != 0u && (hi >= 32 || (kr1 >> hi) == (prefix >> hi)))
+                atomicAdd(&hw[(kr1 >> shift) & dmask], 1);
+            __syncthreads();
+            if (tid < 256) {
+                int t = 0;
+#pragma unroll
+                for (int w = 0; w < kDecWaves; ++w) t += hist[w * 256 + tid];
+                hsum[tid] = t;
+            }
+            __syncthreads();
+            int digit, above;
+            find_digit256(hsum, krem, lane, digit, above);
+            prefix |= static_cast<uint32_t>(digit) << shift;
+            krem -= above;
+        }
+        tau = kmin + prefix;
+        need_eq = krem;
+    }
+    // positions in the ascending kept list: one packed scan of
+    // (keys > tau) << 16 | (keys == tau)
+    const int gt0 = key0 > tau, gt1 = key1 > tau;
+    const int eq0 = key0 == tau, eq1 = key1 == tau;
+    const int packed = ((gt0 + gt1) << 16) | (eq0 + eq1);
+    const int incl = wave_incl_scan(packed);
+    if (lane == 63) red[2 * kDecWaves + wave] = incl;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) before += (w < wave) ? red[2 * kDecWaves + w] : 0;
+    const int excl = before + incl - packed;
+    const int eq_rank = excl & 0xffff;  // this thread's keys == tau are ranked eq_rank, ...
+    int pos = (excl >> 16) + min(eq_rank, need_eq);
+    if (gt0 || (eq0 && eq_rank < need_eq)) {
+        kept[pos] = c0;
+        kept_page[pos] = pg0;
+        ++pos;
+    }
+    if (gt1 || (eq1 && eq_rank + eq0 < need_eq)) {
+        kept[pos] = c0 + 1;
+        kept_page[pos] = pg1;
+    }
+    // the local blocks follow the K picked candidates (their ids are the largest)
+    if (c0 >= NC && c0 < NB) {
+        kept[K + c0 - NC] = c0;
+        kept_page[K + c0 - NC] = pg0;
+    }
+    if (c0 + 1 >= NC && c0 + 1 < NB) {
+        kept[K + c0 + 1 - NC] = c0 + 1;
+        kept_page[K + c0 + 1 - NC] = pg1;
+    }
+    __syncthreads();
+    return n;
+}
+
 // The bf16 kernel: one workgroup of kDecThreads (8 waves) per (sequence, KV
 // head, split), one workgroup per CU.  The split's kept tiles are cut into
 // units of unit_tiles tiles (about one per wave); waves claim units one at a
@@ -119,10 +241,17 @@ __device__ __forceinline__ void merge_waves_and_store(const float* sm, const flo
 // any spare unit.  Each unit leaves its own partial (running max, sum,
 // unnormalised O) in LDS, and the units are merged in unit order at the
 // end, so the result does not depend on which wave took which unit.
-template <int D, int BLK, bool GATE>
+//
+// SEL instance: the workgroup first selects its group's kept blocks from the
+// score row (select_kept; rows of at most kDecodeSelectSlots blocks), with
+// every block's page id requested in the same round trip as the scores, so
+// the split's ids and page ids are in LDS without a further trip.  The first
+// split of each group also writes the kept list to idx_out/cnt_out.
+template <int D, int BLK, bool GATE, bool SEL>
 __global__ __launch_bounds__(kDecThreads)
 __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf16_kernel(
     DecodeParams p) {
+    static_assert(!(GATE && SEL), "the in-workgroup selection writes no bias");
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int NT = D / 16;   // column tiles of the PV product
     constexpr int TPB = BLK / 32;
@@ -154,6 +283,22 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     const int g = lane >> 4;
     const int col = lane & 15;
 
+    // SEL: the length, this thread's two scores and the two blocks' page ids,
+    // requested before the queries (loads past the row read its first entry)
+    int T_v = 0, pg0 = 0, pg1 = 0;
+    float sc0 = 0.f, sc1 = 0.f;
+    if constexpr (SEL) {
+        T_v = load_int_vgpr(c.seq_lens + s);
+        const int c0 = 2 * threadIdx.x;
+        const float* srow = a.scores + static_cast<int64_t>(grp) * a.score_stride;
+        const float2 sv = *reinterpret_cast<const float2*>(srow + (c0 < a.score_stride ? c0 : 0));
+        sc0 = sv.x;
+        sc1 = sv.y;
+        const int32_t* prow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
+        pg0 = prow[c0 < c.max_blocks ? c0 : 0];
+        pg1 = prow[c0 + 1 < c.max_blocks ? c0 + 1 : 0];
+    }
+
     // B operand of S^T = K Q^T: lane (g, col) holds q[head col][32ks + 8g .. +8]
     bf16x8 qb[KS];
     {
@@ -169,21 +314,41 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
 
     // block ids and page ids of this split, resolved once (two dependent
     // round trips for the whole workgroup instead of two per tile)
-    const int32_t* idxrow = a.idx + static_cast<int64_t>(grp) * a.n_max;
-    const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
     const int pb0 = u0 / TPB;
-    const int nblk = (u1 > u0) ? (u1 - 1) / TPB - pb0 + 1 : 0;
-    const int cnt = a.cnt[grp];
-    const int T = c.seq_lens[s];
-    for (int i = threadIdx.x; i < nblk; i += kDecThreads) {
-        const int blk = idxrow[pb0 + i];
-        const bool kept = pb0 + i < cnt;
-        s_blk[i] = kept ? blk : 0;
-        s_page[i] = kept ? ptrow[blk] : 0;
-        if (GATE) s_bias[i] = kept ? a.bias[static_cast<int64_t>(grp) * a.n_max + pb0 + i] * kLog2e : 0.f;
+    // s_blk / s_page hold the split's entries from pb0 on, or (SEL) the
+    // whole kept list
+    const int id0 = SEL ? 0 : pb0;
+    int cnt, T;
+    if constexpr (SEL) {
+        T = __builtin_amdgcn_readfirstlane(T_v);
+        // the selection's scratch lies in the unit partials' LDS, written
+        // only after it
+        cnt = select_kept(a, T, BLK, sc0, sc1, pg0, pg1, reinterpret_cast<int*>(smem), s_blk,
+                          s_page);
+        if (split == 0) {
+            int32_t* orow = a.idx_out + static_cast<int64_t>(grp) * a.n_max;
+            for (int i = threadIdx.x; i < a.n_max; i += kDecThreads)
+                orow[i] = (i < cnt) ? s_blk[i] : -1;
+            if (threadIdx.x == 0) a.cnt_out[grp] = cnt;
+        }
+        if (threadIdx.x == 0) s_next = 0;
+        __syncthreads();
+    } else {
+        const int32_t* idxrow = a.idx + static_cast<int64_t>(grp) * a.n_max;
+        const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
+        const int nblk = (u1 > u0) ? (u1 - 1) / TPB - pb0 + 1 : 0;
+        cnt = a.cnt[grp];
+        T = c.seq_lens[s];
+        for (int i = threadIdx.x; i < nblk; i += kDecThreads) {
+            const int blk = idxrow[pb0 + i];
+            const bool kept = pb0 + i < cnt;
+            s_blk[i] = kept ? blk : 0;
+            s_page[i] = kept ? ptrow[blk] : 0;
+            if (GATE) s_bias[i] = kept ? a.bias[static_cast<int64_t>(grp) * a.n_max + pb0 + i] * kLog2e : 0.f;
+        }
+        if (threadIdx.x == 0) s_next = 0;
+        __syncthreads();
     }
-    if (threadIdx.x == 0) s_next = 0;
-    __syncthreads();
 
     // the kept tiles of the split, in units
     const int uend = min(u1, cnt * TPB);
@@ -212,9 +377,9 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     auto resolve = [&](int u, int64_t& off, int& nvalid, float& b2) __attribute__((always_inline)) {
         const int pi = u / TPB;
         const int r = u - pi * TPB;
-        const int blk = __builtin_amdgcn_readfirstlane(s_blk[pi - pb0]);
-        const int page = __builtin_amdgcn_readfirstlane(s_page[pi - pb0]);
-        b2 = GATE ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_bias[pi - pb0])))
+        const int blk = __builtin_amdgcn_readfirstlane(s_blk[pi - id0]);
+        const int page = __builtin_amdgcn_readfirstlane(s_page[pi - id0]);
+        b2 = GATE ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(s_bias[pi - id0])))
                   : 0.f;
         nvalid = T - (blk * BLK + 32 * r);
         off = (static_cast<int64_t>(page) * c.Hkv + kvh) * static_cast<int64_t>(BLK * D) + 32 * r * D;
@@ -594,6 +759,10 @@ __global__ __launch_bounds__(kCombThreads) void combine_kernel(
 template <int D, int BLK>
 hipError_t launch_bf16(DecodeParams p, hipStream_t stream) {
     const bool gate = p.a.bias != nullptr;
+    const bool sel = p.a.scores != nullptr;
+    if (gate && sel) return hipErrorInvalidValue;
+    // SEL: the whole kept list (at most n_max entries) stays in LDS
+    if (sel) p.max_blocks_per_wg = max(p.max_blocks_per_wg, p.a.n_max);
     // units: about one per wave, of 2 to BSA_DECODE_MAX_UNIT tiles (fewer,
     // longer units mean fewer partials to flush and merge, and waves that
     // the hardware serves faster still take the spare units); longer units
@@ -610,12 +779,22 @@ hipError_t launch_bf16(DecodeParams p, hipStream_t stream) {
     ut = max(ut, (tiles + slots - 1) / slots);
     p.unit_tiles = ut;
     p.max_units = (tiles + ut - 1) / ut;
+    // SEL: the selection's scratch lies in the unit partials' slots
+    if (sel) {
+        const int sel_bytes = static_cast<int>(sizeof(int)) * kSelScratchInts;
+        p.max_units = max(p.max_units, (sel_bytes + unit_bytes - 1) / unit_bytes);
+    }
     const size_t shm = static_cast<size_t>(unit_bytes) * p.max_units + id_bytes;
     dim3 grid(p.a.splits, p.c.B * p.c.Hkv);
     if (gate)
-        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, true>), grid, dim3(kDecThreads), shm, stream, p);
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, true, false>), grid, dim3(kDecThreads), shm,
+                           stream, p);
+    else if (sel)
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, true>), grid, dim3(kDecThreads), shm,
+                           stream, p);
     else
-        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false>), grid, dim3(kDecThreads), shm, stream, p);
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, false>), grid, dim3(kDecThreads), shm,
+                           stream, p);
     return hipGetLastError();
 }
 
@@ -684,6 +863,8 @@ hipError_t launch_decode(const CacheArgs& c, const DecodeArgs& a, hipStream_t st
     const int tpb = c.block / 32;
     const int tiles = (a.n_max * tpb + a.splits - 1) / a.splits;
     DecodeParams p{c, a, tiles / tpb + 2, 0, 0};
+    if (a.scores && (c.dtype != kBF16 || c.max_blocks > kDecodeSelectSlots))
+        return hipErrorInvalidValue;
     hipError_t err;
     if (c.dtype == kBF16)
         err = c.d == 64 ? launch_bf16_d<64>(p, stream) : launch_bf16_d<128>(p, stream);

@@ -56,22 +56,6 @@ constexpr int kScoreIters = BSA_SCORE_ITERS;
 constexpr int kTopnThreads = 1024;
 constexpr int kTopnWaves = kTopnThreads / kWave;
 constexpr int kAliveCap = 2048;  // keys gathered after the first radix pass
-// word 3 of a raw buffer descriptor on gfx9-family parts (32-bit data
-// format, no swizzle): stores through it are range-checked against the
-// descriptor's byte count
-constexpr int kBufferWord3 = 0x00020000;
-
-// One int read with a vector (buffer) load, left in a VGPR until the caller
-// takes it with readfirstlane at its use: the load joins the round trip of
-// the vector loads issued with it, where a scalar load would be placed at
-// its first use and waited for on its own.
-__device__ __forceinline__ int load_int_vgpr(const int32_t* p) {
-    return __builtin_amdgcn_raw_buffer_load_b32(
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(p), 0,
-                                          static_cast<int>(sizeof(int32_t)), kBufferWord3),
-        0, 0, 0);
-}
-
 struct ScoreParams {
     CacheArgs c;
     SelectArgs s;
@@ -583,26 +567,7 @@ __global__ __launch_bounds__(kTopnThreads) void topn_kernel(TopnParams p) {
         // returns the digit holding the krem-th largest alive key and how
         // many alive keys lie in higher digits
         auto find_digit = [&](const int* h, int& digit, int& above) __attribute__((always_inline)) {
-            int c4[4], hv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) hv[i] = h[255 - 4 * lane - i];
-            c4[0] = hv[0];
-#pragma unroll
-            for (int i = 1; i < 4; ++i) c4[i] = c4[i - 1] + hv[i];
-            const int incl = wave_incl_scan(c4[3]);
-            const int excl = incl - c4[3];
-            int found_i = -1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ge = excl + c4[i];  // keys whose digit >= this one
-                if (ge >= krem && ge - hv[i] < krem) found_i = i;
-            }
-            const uint64_t bal = __ballot(found_i >= 0);
-            const int src = __ffsll(static_cast<unsigned long long>(bal)) - 1;  // exactly one lane
-            const int my_digit = 255 - 4 * lane - (found_i < 0 ? 0 : found_i);
-            const int my_above = excl + (found_i <= 0 ? 0 : c4[found_i - 1]);
-            digit = __builtin_amdgcn_readlane(my_digit, src);
-            above = __builtin_amdgcn_readlane(my_above, src);
+            find_digit256(h, krem, lane, digit, above);
         };
         // one radix pass over every key of the workgroup
         auto block_pass = [&]() __attribute__((always_inline)) {
@@ -895,6 +860,17 @@ hipError_t launch_select(const CacheArgs& c, const SelectArgs& s, hipStream_t st
                                      : launch_score_d<kF32, kMeanPool>(sp, stream);
     if (err != hipSuccess) return err;
     return launch_topn(c, s, stream);
+}
+
+hipError_t launch_append_score_only(const CacheArgs& c, const void* k_new, const void* v_new,
+                                    const SelectArgs& s, hipStream_t stream) {
+    ScoreParams sp{c, s, score_stride(c.max_blocks)};
+    KvWriteParams kp{c, kModeAppend, k_new, v_new, 1, nullptr};
+    if (c.dtype == kBF16)
+        return c.desc_kind == kMinMax ? launch_append_score_d<kBF16, kMinMax>(sp, kp, stream)
+                                      : launch_append_score_d<kBF16, kMeanPool>(sp, kp, stream);
+    return c.desc_kind == kMinMax ? launch_append_score_d<kF32, kMinMax>(sp, kp, stream)
+                                  : launch_append_score_d<kF32, kMeanPool>(sp, kp, stream);
 }
 
 hipError_t launch_append_select(const CacheArgs& c, const void* k_new, const void* v_new,

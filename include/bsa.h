@@ -123,7 +123,8 @@ typedef enum bsa_desc_kind {
 typedef enum bsa_op {
     BSA_OP_SELECT = 1,
     BSA_OP_DECODE = 2,
-    BSA_OP_RECTIFY = 3
+    BSA_OP_RECTIFY = 3,
+    BSA_OP_STEP = 4     /* bsa_append_select_decode, by n_max */
 } bsa_op;
 
 /* Problem shape.  Supported: 1 <= Hq/Hkv <= 16 with Hq % Hkv == 0;
@@ -286,6 +287,36 @@ BSA_API bsa_status bsa_sparse_decode(const bsa_layout* layout, const bsa_cache* 
                              void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * bsa_append_select_decode -- one whole decode step of one layer:
+ * bsa_append_select (append one token per sequence, score, keep the top-n)
+ * then bsa_sparse_decode over the kept blocks (with
+ * bsa_sparse_decode_gated's log-gate bias when params->gate_bias is set).
+ * Same references as those calls ("Rectified Sparse Attention ...",
+ * Summary and Key points; "Simple Attention Sparsification", Method).
+ * Results (the cache, idx, cnt, gate_bias, o, lse) are identical to those
+ * calls made in that order with the same arguments.  For bf16 caches of at
+ * most 1024 blocks per sequence (max_blocks <= 1024) without gate_bias, the
+ * selection runs inside the decode launch: every decode workgroup selects
+ * its group's kept blocks from the scores, which saves the top-n launch and
+ * a dependent round trip; other cases make the four launches of the two
+ * calls.
+ * k_new, v_new: [B][Hkv][1][d]; q: [B][Hq][d] (KV dtype; the caller has
+ *   already advanced seq_lens by one).  idx, cnt: OUT, as bsa_select_blocks
+ *   writes them (row length params->n_max).  o, lse: OUT, as
+ *   bsa_sparse_decode.
+ * ws: at least bsa_workspace_size(layout, BSA_OP_STEP, params->n_max) bytes
+ *   (the scores, then the decode's split partials; no initialisation).
+ * Errors: those of bsa_append_select and bsa_sparse_decode.
+ * ------------------------------------------------------------------------- */
+BSA_API bsa_status bsa_append_select_decode(const bsa_layout* layout,
+                             const bsa_cache* cache, const void* k_new,
+                             const void* v_new, const void* q,
+                             const bsa_select_params* params, int32_t* idx,
+                             int32_t* cnt, float softmax_scale, void* o,
+                             float* lse, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * bsa_sparse_decode_gated -- bsa_sparse_decode with an additive logit bias
  * per kept block ("Simple Attention Sparsification", Method: the o_SAS
  * equation, softmax(q K_S^T + log g_S) V_S over the kept blocks S):
@@ -358,7 +389,7 @@ BSA_API bsa_status bsa_rectify_chunk(const bsa_layout* layout, const bsa_cache* 
                              hipStream_t stream);
 
 /* Workspace bytes needed by an operation (op = bsa_op), for the given
- * n_max (SELECT, DECODE) or f (RECTIFY).  Returns 0 for an invalid layout or
+ * n_max (SELECT, DECODE, STEP) or f (RECTIFY).  Returns 0 for an invalid layout or
  * op.  Host-only; makes no HIP call. */
 BSA_API size_t bsa_workspace_size(const bsa_layout* layout, int32_t op,
                           int32_t n_max_or_f);

@@ -168,6 +168,34 @@ def test_append_select_validation():
     assert call(L=L_ok(d=96)) == bsa.ERR_UNSUPPORTED
 
 
+def test_append_select_decode_validation():
+    L = L_ok()
+    C = bsa.c_cache(0x1000, 0x1000, 0x1000, 0x1000, 0x1000)
+    p = ctypes.c_void_p(0x1000)
+    lib = bsa.lib()
+    P = bsa.SelectParams(sparsity_bp=9000, n_local=2, n_max=10)
+    need = bsa.workspace_size(L, bsa.OP_STEP, 10)
+    # the step's workspace holds the scores, then the decode's partials
+    assert need == (bsa.workspace_size(L, bsa.OP_SELECT, 10)
+                    + bsa.workspace_size(L, bsa.OP_DECODE, 10))
+
+    def call(L=L, k=p, v=p, P=P, o=p, scale=0.1, ws_bytes=need):
+        return lib.bsa_append_select_decode(ctypes.byref(L.c()), ctypes.byref(C), k, v, p,
+                                            ctypes.byref(P.c()), p, p, scale, o, p, p, ws_bytes,
+                                            None)
+    assert call(k=None) == bsa.ERR_NULL
+    assert call(o=None) == bsa.ERR_NULL
+    assert call(P=bsa.SelectParams(sparsity_bp=9000, n_local=0, n_max=10)) == bsa.ERR_PARAM
+    assert call(P=bsa.SelectParams(sparsity_bp=9000, n_local=2, n_max=5)) == bsa.ERR_PARAM
+    # n_max beyond the layout's capacity (the decode's bound)
+    assert call(P=bsa.SelectParams(sparsity_bp=9000, n_local=2, n_max=101),
+                ws_bytes=1 << 30) == bsa.ERR_PARAM
+    assert call(scale=0.0) == bsa.ERR_PARAM
+    assert call(scale=float("inf")) == bsa.ERR_PARAM
+    assert call(ws_bytes=need - 1) == bsa.ERR_WORKSPACE
+    assert call(L=L_ok(d=96)) == bsa.ERR_UNSUPPORTED
+
+
 class _FakeDev:
     """Stands in for a device tensor in validation calls that never launch."""
     def data_ptr(self):

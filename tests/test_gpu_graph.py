@@ -2,7 +2,8 @@
 eager result of the same inputs (the library records no memset nodes;
 replays are interleaved with eager work and synchronisations).  Two step
 forms: the separate calls, and the fused append + select writing the
-log-gate bias with the gated decode."""
+log-gate bias with the gated decode; and the whole step as one
+bsa_append_select_decode call (selection inside the decode launch)."""
 import math
 
 import numpy as np
@@ -15,7 +16,7 @@ from test_gpu_parity import make_inputs
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("form", ["separate", "fused_gated"])
+@pytest.mark.parametrize("form", ["separate", "fused_gated", "one_call"])
 def test_graph_replays_match_eager(form):
     import torch
     d, blk, f = 128, 64, 32
@@ -33,7 +34,8 @@ def test_graph_replays_match_eager(form):
     kr = torch.from_numpy(rng.standard_normal((2, 2, f, d), dtype=np.float32)).to(dev, torch.bfloat16)
     vr = torch.from_numpy(rng.standard_normal((2, 2, f, d), dtype=np.float32)).to(dev, torch.bfloat16)
     ws_bytes = max(bsa.workspace_size(L, op, n) for op, n in
-                   [(bsa.OP_SELECT, P.n_max), (bsa.OP_DECODE, P.n_max), (bsa.OP_RECTIFY, f)])
+                   [(bsa.OP_SELECT, P.n_max), (bsa.OP_DECODE, P.n_max), (bsa.OP_RECTIFY, f),
+                    (bsa.OP_STEP, P.n_max)])
 
     def fresh():
         cache = bsa.allocate_cache(L, page_table=random_page_table(L, 8))
@@ -57,6 +59,9 @@ def test_graph_replays_match_eager(form):
             bsa.select_blocks(L, cache, qd, P, b["idx"], b["cnt"], b["ws"])
             bsa.sparse_decode(L, cache, qd, b["idx"], b["cnt"], P.n_max, 1 / math.sqrt(d), b["o"],
                               b["lse"], b["ws"])
+        elif form == "one_call":
+            bsa.append_select_decode(L, cache, kn, vn, qd, P, b["idx"], b["cnt"], 1 / math.sqrt(d),
+                                     b["o"], b["lse"], b["ws"])
         else:
             Pg = bsa.SelectParams(sparsity_bp=8000, n_local=2, n_min=4, n_max=P.n_max,
                                   gate_tau=0.02, gate_bias=b["bias"])
