@@ -12,7 +12,7 @@ set cannot stay resident in the 256 MB last-level cache):
                                    in the scoring launch)
              + bsa_sparse_decode   (split-K attention over the kept blocks,
                                     log-sum-exp merge) in one call; for rows
-                                    of at most 1024 blocks the top-n runs in
+                                    of at most 4096 blocks the top-n runs in
                                     the decode launch
              bsa_rectify_chunk     (every f steps, workloads with rectification)
   (--step-form separate times the two calls instead).

@@ -76,8 +76,8 @@ struct DecodeArgs {
 hipError_t launch_decode(const CacheArgs& c, const DecodeArgs& a, hipStream_t stream);
 int decode_splits(const CacheArgs& c, int n_max);
 // Blocks per sequence up to which the decode kernel can select in-workgroup
-// (two per thread).
-constexpr int kDecodeSelectSlots = 1024;
+// (up to eight per thread).
+constexpr int kDecodeSelectSlots = 4096;
 
 struct RectifyArgs {
     const void* q;      // [B][Hq][f][d]

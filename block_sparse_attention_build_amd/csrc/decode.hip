@@ -112,45 +112,55 @@ __device__ __forceinline__ void merge_waves_and_store(const float* sm, const flo
     }
 }
 
-// In-workgroup selection, for rows of at most kDecodeSelectSlots blocks
-// (thread t holds blocks 2t and 2t + 1).  The rule is the top-n kernel's
-// ("Rectified Sparse Attention ...", Key points: dynamic top-n with local
-// blocks and a minimum count; "Simple Attention Sparsification", Method:
-// discrete Top-K with the current block always kept): n = block_count(NB),
-// the nl = min(n_local, NB) last blocks, and the n - nl candidates of largest
-// score (ties to the lower index), found by an MSB-first radix select over
-// order-preserving uint32 keys.  The kept ids and their page ids go to
-// kept/kept_page (LDS, ascending); returns n.  scratch: LDS,
-// kSelScratchInts ints, free again on return.  Ends with a barrier.
+// In-workgroup selection, for rows of at most KPT * kDecThreads blocks
+// (thread t holds blocks KPT*t .. KPT*t + KPT - 1).  The rule is the top-n
+// kernel's ("Rectified Sparse Attention ...", Key points: dynamic top-n with
+// local blocks and a minimum count; "Simple Attention Sparsification",
+// Method: discrete Top-K with the current block always kept):
+// n = block_count(NB), the nl = min(n_local, NB) last blocks, and the n - nl
+// candidates of largest score (ties to the lower index), found by an
+// MSB-first radix select over order-preserving uint32 keys.  The kept ids
+// and their page ids go to kept/kept_page (LDS, ascending); returns n.
+// scratch: LDS, kSelScratchInts ints, free again on return.  Ends with a
+// barrier.
 constexpr int kDecWaves = kDecThreads / kWave;
-constexpr int kSelScratchInts = kDecWaves * 256 + 256 + 3 * kDecWaves;
-static_assert(2 * kDecThreads == kDecodeSelectSlots, "two blocks per thread");
+constexpr int kSelAliveCap = 1024;  // keys gathered after the first radix pass
+constexpr int kSelScratchInts = kDecWaves * 256 + 256 + 3 * kDecWaves + 4 + kSelAliveCap;
+static_assert(8 * kDecThreads == kDecodeSelectSlots, "at most eight blocks per thread");
 
-__device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block, float sc0,
-                                           float sc1, int pg0, int pg1, int* scratch, int* kept,
-                                           int* kept_page) {
+template <int KPT>
+__device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block,
+                                           const float (&sc)[KPT], const int (&pg)[KPT],
+                                           int* scratch, int* kept, int* kept_page) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     int* hist = scratch;                  // [kDecWaves][256] digit counts, one per wave
     int* hsum = hist + kDecWaves * 256;   // [256] their sum
     int* red = hsum + 256;                // [3][kDecWaves] min, max, scan totals
+    int* misc = red + 3 * kDecWaves;      // [4] alive-list length, prefix, keys left
+    uint32_t* alive = reinterpret_cast<uint32_t*>(misc + 4);  // [kSelAliveCap] key - kmin
     const int NB = (T + block - 1) / block;
     const int nl = min(a.n_local, NB);
     const int NC = NB - nl;
     const int n = block_count(NB, block, a.budget_tokens, a.sparsity_bp, a.n_local, a.n_min);
     const int K = n - nl;  // candidates to pick (0 <= K <= NC)
-    const int c0 = 2 * tid;
+    const int base = KPT * tid;
     // slots that are not candidates hold the key 0, below every real key
-    const uint32_t key0 = (c0 < NC) ? float_key(sc0) : 0u;
-    const uint32_t key1 = (c0 + 1 < NC) ? float_key(sc1) : 0u;
+    uint32_t key[KPT];
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) key[r] = (base + r < NC) ? float_key(sc[r]) : 0u;
     // keys > tau are taken, and the first need_eq keys == tau (by index):
     // K = 0 takes nothing (no key exceeds 0xffffffff), K = NC every candidate
     uint32_t tau = (K == 0) ? 0xffffffffu : 0u;
     int need_eq = 0;
     if (K > 0 && K < NC) {  // uniform
-        uint32_t lmin = min(key0 - 1u, key1 - 1u);  // the key 0 wraps to the top
-        uint32_t lmax = max(key0, key1);
+        uint32_t lmin = 0xffffffffu, lmax = 0u;
+#pragma unroll
+        for (int r = 0; r < KPT; ++r) {
+            lmin = min(lmin, key[r] - 1u);  // the key 0 wraps to the top
+            lmax = max(lmax, key[r]);
+        }
         lmin = wave_min_u32(lmin);
         lmax = wave_max_u32(lmax);
         if (lane == 0) {
@@ -169,8 +179,10 @@ __device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block
         uint32_t prefix = 0;  // of key - kmin, above the current digit
         int krem = K;         // keys still to take at or below the prefix
         int shift = (range == 0u) ? 0 : 32 - __clz(static_cast<int>(range));
-        const uint32_t kr0 = key0 - kmin, kr1 = key1 - kmin;
-        while (shift > 0) {  // uniform
+        // a wave whose first slot is past the candidates holds only keys 0
+        const bool live = wave * kWave * KPT < NC;  // wave-uniform
+        // one radix pass over every key of the workgroup; returns the digit
+        auto block_pass = [&]() __attribute__((always_inline)) {
             const int dbits = min(8, shift);
             shift -= dbits;
             const int hi = shift + dbits;
@@ -178,10 +190,15 @@ __device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block
             int* hw = hist + wave * 256;
 #pragma unroll
             for (int i = 0; i < 4; ++i) hw[lane + 64 * i] = 0;  // nobody reads it now
-            if (key0 != 0u && (hi >= 32 || (kr0 >> hi) == (prefix >> hi)))
-                atomicAdd(&hw[(kr0 >> shift) & dmask], 1);
-            if (key1 != 0u && (hi >= 32 || (kr1 >> hi) == (prefix >> hi)))
-                atomicAdd(&hw[(kr1 >> shift) & dmask], 1);
+            if (live) {
+#pragma unroll
+                for (int r = 0; r < KPT; ++r) {
+                    const uint32_t kr = key[r] - kmin;
+                    if (key[r] != 0u && (hi >= 32 || (kr >> hi) == (prefix >> hi)))
+                        atomicAdd(&hw[(kr >> shift) & dmask], 1);
+                }
+            }
+            if (tid == 0) misc[0] = 0;  // the alive list below starts empty
             __syncthreads();
             if (tid < 256) {
                 int t = 0;
@@ -194,15 +211,79 @@ __device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block
             find_digit256(hsum, krem, lane, digit, above);
             prefix |= static_cast<uint32_t>(digit) << shift;
             krem -= above;
+            return digit;
+        };
+        // The first pass runs over every key.  The keys still alive after it
+        // (those in the threshold's digit, usually a small fraction) are
+        // gathered into LDS and wave 0 finishes the remaining passes on that
+        // list alone, with no workgroup barriers; a list too long for the
+        // buffer keeps to whole-workgroup passes.
+        if (shift > 0) {
+            const int d1 = block_pass();
+            const int n_alive = hsum[d1];
+            if (shift > 0 && n_alive <= kSelAliveCap) {
+                if (live) {
+                    // list slots: a lane mask of the alive keys, a wave prefix
+                    // of the lane counts and one LDS atomic per wave
+                    uint32_t am = 0u;
+#pragma unroll
+                    for (int r = 0; r < KPT; ++r) {
+                        const uint32_t kr = key[r] - kmin;
+                        am |= (key[r] != 0u && (kr >> shift) == (prefix >> shift)) ? (1u << r) : 0u;
+                    }
+                    const int cnt_l = __builtin_popcount(am);
+                    const int incl_l = wave_incl_scan(cnt_l);
+                    int wbase = 0;
+                    if (lane == 63) wbase = atomicAdd(&misc[0], incl_l);
+                    int at = __builtin_amdgcn_readlane(wbase, 63) + incl_l - cnt_l;
+#pragma unroll
+                    for (int r = 0; r < KPT; ++r)
+                        if (am & (1u << r)) alive[at++] = key[r] - kmin;
+                }
+                __syncthreads();
+                if (wave == 0) {
+                    while (shift > 0) {
+                        const int dbits = min(8, shift);
+                        shift -= dbits;
+                        const int hi = shift + dbits;
+                        int* hw = hist;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) hw[lane + 64 * i] = 0;
+                        for (int i = lane; i < n_alive; i += kWave) {
+                            const uint32_t kr = alive[i];
+                            if ((kr >> hi) == (prefix >> hi))
+                                atomicAdd(&hw[(kr >> shift) & ((1u << dbits) - 1u)], 1);
+                        }
+                        int digit, above;
+                        find_digit256(hw, krem, lane, digit, above);
+                        prefix |= static_cast<uint32_t>(digit) << shift;
+                        krem -= above;
+                    }
+                    if (lane == 0) {
+                        misc[1] = static_cast<int>(prefix);
+                        misc[2] = krem;
+                    }
+                }
+                __syncthreads();
+                prefix = static_cast<uint32_t>(misc[1]);
+                krem = misc[2];
+                shift = 0;
+            }
+            while (shift > 0) block_pass();
         }
         tau = kmin + prefix;
         need_eq = krem;
     }
     // positions in the ascending kept list: one packed scan of
-    // (keys > tau) << 16 | (keys == tau)
-    const int gt0 = key0 > tau, gt1 = key1 > tau;
-    const int eq0 = key0 == tau, eq1 = key1 == tau;
-    const int packed = ((gt0 + gt1) << 16) | (eq0 + eq1);
+    // (keys > tau) << 16 | (keys == tau), the keys kept as bit masks
+    uint32_t gt_m = 0u, eq_m = 0u;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+        gt_m |= (key[r] > tau) ? (1u << r) : 0u;
+        eq_m |= (key[r] == tau) ? (1u << r) : 0u;
+    }
+    const int n_eq = __builtin_popcount(eq_m);
+    const int packed = (__builtin_popcount(gt_m) << 16) | n_eq;
     const int incl = wave_incl_scan(packed);
     if (lane == 63) red[2 * kDecWaves + wave] = incl;
     __syncthreads();
@@ -212,23 +293,31 @@ __device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block
     const int excl = before + incl - packed;
     const int eq_rank = excl & 0xffff;  // this thread's keys == tau are ranked eq_rank, ...
     int pos = (excl >> 16) + min(eq_rank, need_eq);
-    if (gt0 || (eq0 && eq_rank < need_eq)) {
-        kept[pos] = c0;
-        kept_page[pos] = pg0;
-        ++pos;
+    uint32_t take_m = gt_m;  // and those equal keys ranked below need_eq
+    for (int k = max(0, min(need_eq - eq_rank, n_eq)); k > 0; --k) {
+        take_m |= eq_m & (0u - eq_m);
+        eq_m &= eq_m - 1u;
     }
-    if (gt1 || (eq1 && eq_rank + eq0 < need_eq)) {
-        kept[pos] = c0 + 1;
-        kept_page[pos] = pg1;
+    // the taken keys, lowest index first; a key's page id is picked out of
+    // the registers with a select chain (no dynamic register indexing)
+    while (take_m != 0u) {
+        const int rr = __builtin_ctz(take_m);
+        int page = pg[0];
+#pragma unroll
+        for (int i = 1; i < KPT; ++i) page = (rr == i) ? pg[i] : page;
+        kept[pos] = base + rr;
+        kept_page[pos] = page;
+        ++pos;
+        take_m &= take_m - 1u;
     }
     // the local blocks follow the K picked candidates (their ids are the largest)
-    if (c0 >= NC && c0 < NB) {
-        kept[K + c0 - NC] = c0;
-        kept_page[K + c0 - NC] = pg0;
-    }
-    if (c0 + 1 >= NC && c0 + 1 < NB) {
-        kept[K + c0 + 1 - NC] = c0 + 1;
-        kept_page[K + c0 + 1 - NC] = pg1;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) {
+        const int c = base + r;
+        if (c >= NC && c < NB) {
+            kept[K + c - NC] = c;
+            kept_page[K + c - NC] = pg[r];
+        }
     }
     __syncthreads();
     return n;
@@ -242,15 +331,17 @@ __device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block
 // unnormalised O) in LDS, and the units are merged in unit order at the
 // end, so the result does not depend on which wave took which unit.
 //
-// SEL instance: the workgroup first selects its group's kept blocks from the
-// score row (select_kept; rows of at most kDecodeSelectSlots blocks), with
-// every block's page id requested in the same round trip as the scores, so
-// the split's ids and page ids are in LDS without a further trip.  The first
-// split of each group also writes the kept list to idx_out/cnt_out.
-template <int D, int BLK, bool GATE, bool SEL>
+// SELK > 0: the workgroup first selects its group's kept blocks from the
+// score row (select_kept, SELK blocks per thread), with every block's page id
+// requested in the same round trip as the scores, so the split's ids and
+// page ids are in LDS without a further trip.  The first split of each group
+// also writes the kept list to idx_out/cnt_out.
+template <int D, int BLK, bool GATE, int SELK>
 __global__ __launch_bounds__(kDecThreads)
 __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf16_kernel(
     DecodeParams p) {
+    constexpr bool SEL = SELK > 0;
+    constexpr int NK = SEL ? SELK : 1;
     static_assert(!(GATE && SEL), "the in-workgroup selection writes no bias");
     constexpr int KS = D / 32;   // k-steps of the QK product
     constexpr int NT = D / 16;   // column tiles of the PV product
@@ -283,20 +374,33 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     const int g = lane >> 4;
     const int col = lane & 15;
 
-    // SEL: the length, this thread's two scores and the two blocks' page ids,
-    // requested before the queries (loads past the row read its first entry)
-    int T_v = 0, pg0 = 0, pg1 = 0;
-    float sc0 = 0.f, sc1 = 0.f;
+    // SEL: the length, this thread's NK scores and their blocks' page ids,
+    // requested before the queries (loads past the row read its first
+    // entries; the row stride is a multiple of 4)
+    int T_v = 0;
+    float sc[NK];
+    int pg[NK];
     if constexpr (SEL) {
         T_v = load_int_vgpr(c.seq_lens + s);
-        const int c0 = 2 * threadIdx.x;
+        const int base = NK * threadIdx.x;
         const float* srow = a.scores + static_cast<int64_t>(grp) * a.score_stride;
-        const float2 sv = *reinterpret_cast<const float2*>(srow + (c0 < a.score_stride ? c0 : 0));
-        sc0 = sv.x;
-        sc1 = sv.y;
+        if constexpr (NK >= 4) {
+#pragma unroll
+            for (int r = 0; r < NK; r += 4) {
+                const floatx4 v =
+                    *reinterpret_cast<const floatx4*>(srow + (base + r < a.score_stride ? base + r : 0));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) sc[r + k] = v[k];
+            }
+        } else {
+            static_assert(NK == 2, "2, 4 or 8 blocks per thread");
+            const float2 v = *reinterpret_cast<const float2*>(srow + (base < a.score_stride ? base : 0));
+            sc[0] = v.x;
+            sc[1] = v.y;
+        }
         const int32_t* prow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
-        pg0 = prow[c0 < c.max_blocks ? c0 : 0];
-        pg1 = prow[c0 + 1 < c.max_blocks ? c0 + 1 : 0];
+#pragma unroll
+        for (int r = 0; r < NK; ++r) pg[r] = prow[base + r < c.max_blocks ? base + r : 0];
     }
 
     // B operand of S^T = K Q^T: lane (g, col) holds q[head col][32ks + 8g .. +8]
@@ -323,8 +427,7 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
         T = __builtin_amdgcn_readfirstlane(T_v);
         // the selection's scratch lies in the unit partials' LDS, written
         // only after it
-        cnt = select_kept(a, T, BLK, sc0, sc1, pg0, pg1, reinterpret_cast<int*>(smem), s_blk,
-                          s_page);
+        cnt = select_kept<NK>(a, T, BLK, sc, pg, reinterpret_cast<int*>(smem), s_blk, s_page);
         if (split == 0) {
             int32_t* orow = a.idx_out + static_cast<int64_t>(grp) * a.n_max;
             for (int i = threadIdx.x; i < a.n_max; i += kDecThreads)
@@ -787,13 +890,19 @@ hipError_t launch_bf16(DecodeParams p, hipStream_t stream) {
     const size_t shm = static_cast<size_t>(unit_bytes) * p.max_units + id_bytes;
     dim3 grid(p.a.splits, p.c.B * p.c.Hkv);
     if (gate)
-        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, true, false>), grid, dim3(kDecThreads), shm,
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, true, 0>), grid, dim3(kDecThreads), shm,
                            stream, p);
-    else if (sel)
-        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, true>), grid, dim3(kDecThreads), shm,
+    else if (!sel)
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, 0>), grid, dim3(kDecThreads), shm,
+                           stream, p);
+    else if (p.c.max_blocks <= 2 * kDecThreads)
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, 2>), grid, dim3(kDecThreads), shm,
+                           stream, p);
+    else if (p.c.max_blocks <= 4 * kDecThreads)
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, 4>), grid, dim3(kDecThreads), shm,
                            stream, p);
     else
-        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, false>), grid, dim3(kDecThreads), shm,
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, 8>), grid, dim3(kDecThreads), shm,
                            stream, p);
     return hipGetLastError();
 }

@@ -295,7 +295,7 @@ BSA_API bsa_status bsa_sparse_decode(const bsa_layout* layout, const bsa_cache* 
  * Summary and Key points; "Simple Attention Sparsification", Method).
  * Results (the cache, idx, cnt, gate_bias, o, lse) are identical to those
  * calls made in that order with the same arguments.  For bf16 caches of at
- * most 1024 blocks per sequence (max_blocks <= 1024) without gate_bias, the
+ * most 4096 blocks per sequence (max_blocks <= 4096) without gate_bias, the
  * selection runs inside the decode launch: every decode workgroup selects
  * its group's kept blocks from the scores, which saves the top-n launch and
  * a dependent round trip; other cases make the four launches of the two
