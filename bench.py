@@ -12,8 +12,8 @@ set cannot stay resident in the 256 MB last-level cache):
                                    in the scoring launch)
              + bsa_sparse_decode   (split-K attention over the kept blocks,
                                     log-sum-exp merge) in one call; for rows
-                                    of at most 4096 blocks the top-n runs in
-                                    the decode launch
+                                    of at most 8192 candidate blocks the top-n
+                                    runs in the decode launch
              bsa_rectify_chunk     (every f steps, workloads with rectification)
   (--step-form separate times the two calls instead).
 Queries, appended tokens and re-encoded keys/values are fresh per step and

@@ -431,7 +431,7 @@ bsa_status bsa_append_select_decode(const bsa_layout* layout, const bsa_cache* c
     a.lse_part = reinterpret_cast<float*>(dws + w.lse_part);
     a.o = o;
     a.lse = lse;
-    const bool in_wg = c.dtype == kBF16 && !params->gate_bias && c.max_blocks <= kDecodeSelectSlots;
+    const bool in_wg = !params->gate_bias && decode_selects(c, params->n_local, params->n_max);
     if (!in_wg) {
         if ((st = hip_status(launch_append_select(c, k_new, v_new, s, stream))) != BSA_OK)
             return st;

@@ -75,9 +75,14 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const CacheArgs& c, const DecodeArgs& a, hipStream_t stream);
 int decode_splits(const CacheArgs& c, int n_max);
-// Blocks per sequence up to which the decode kernel can select in-workgroup
-// (up to eight per thread).
-constexpr int kDecodeSelectSlots = 4096;
+// In-workgroup selection: candidate blocks per sequence (max_blocks minus the
+// local blocks) up to which the decode kernel can select (up to sixteen per
+// thread), and the longest kept list it holds in LDS beside the unit
+// partials (so that the decode's units are cut as in bsa_sparse_decode).
+constexpr int kDecodeSelectSlots = 8192;
+constexpr int kDecodeSelectMaxKept = 4096;
+// Whether launch_decode can select in-workgroup for this layout.
+bool decode_selects(const CacheArgs& c, int n_local, int n_max);
 
 struct RectifyArgs {
     const void* q;      // [B][Hq][f][d]

@@ -112,44 +112,49 @@ __device__ __forceinline__ void merge_waves_and_store(const float* sm, const flo
     }
 }
 
-// In-workgroup selection, for rows of at most KPT * kDecThreads blocks
-// (thread t holds blocks KPT*t .. KPT*t + KPT - 1).  The rule is the top-n
-// kernel's ("Rectified Sparse Attention ...", Key points: dynamic top-n with
-// local blocks and a minimum count; "Simple Attention Sparsification",
-// Method: discrete Top-K with the current block always kept):
-// n = block_count(NB), the nl = min(n_local, NB) last blocks, and the n - nl
-// candidates of largest score (ties to the lower index), found by an
-// MSB-first radix select over order-preserving uint32 keys.  The kept ids
-// and their page ids go to kept/kept_page (LDS, ascending); returns n.
-// scratch: LDS, kSelScratchInts ints, free again on return.  Ends with a
-// barrier.
+// In-workgroup selection, for rows of at most KPT * kDecThreads candidate
+// blocks.  Thread t holds the keys of blocks t, t + kDecThreads, ... (row r
+// of the thread is block t + r * kDecThreads), so every score and page-id
+// load of a row is one coalesced wave load.  The rule is the top-n kernel's
+// ("Rectified Sparse Attention ...", Key points: dynamic top-n with local
+// blocks and a minimum count; "Simple Attention Sparsification", Method:
+// discrete Top-K with the current block always kept): n = block_count(NB),
+// the nl = min(n_local, NB) last blocks, and the n - nl candidates of largest
+// score (ties to the lower index), found by an MSB-first radix select over
+// order-preserving uint32 keys.  The kept ids and their page ids go to
+// kept/kept_page (LDS, ascending); returns n.  pg[r]: page id of the thread's
+// block in row r; lpg: page id of local block tid (tid < nl).  scratch: LDS,
+// kSelScratchInts ints, free again on return.  Ends with a barrier.
 constexpr int kDecWaves = kDecThreads / kWave;
 constexpr int kSelAliveCap = 1024;  // keys gathered after the first radix pass
-constexpr int kSelScratchInts = kDecWaves * 256 + 256 + 3 * kDecWaves + 4 + kSelAliveCap;
-static_assert(8 * kDecThreads == kDecodeSelectSlots, "at most eight blocks per thread");
+constexpr int kSelMaxRows = 16;     // candidate rows per thread
+constexpr int kSelScratchInts =
+    kDecWaves * 256 + 256 + 2 * kDecWaves + 4 + kSelAliveCap + kSelMaxRows * kDecWaves;
+static_assert(kSelMaxRows * kDecThreads == kDecodeSelectSlots, "candidate capacity");
 
 template <int KPT>
 __device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block,
-                                           const float (&sc)[KPT], const int (&pg)[KPT],
+                                           const float (&sc)[KPT], const int (&pg)[KPT], int lpg,
                                            int* scratch, int* kept, int* kept_page) {
+    static_assert(KPT <= kSelMaxRows, "rows per thread");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     int* hist = scratch;                  // [kDecWaves][256] digit counts, one per wave
     int* hsum = hist + kDecWaves * 256;   // [256] their sum
-    int* red = hsum + 256;                // [3][kDecWaves] min, max, scan totals
-    int* misc = red + 3 * kDecWaves;      // [4] alive-list length, prefix, keys left
+    int* red = hsum + 256;                // [2][kDecWaves] min, max
+    int* misc = red + 2 * kDecWaves;      // [4] alive-list length, prefix, keys left
     uint32_t* alive = reinterpret_cast<uint32_t*>(misc + 4);  // [kSelAliveCap] key - kmin
+    int* rowcnt = misc + 4 + kSelAliveCap;  // [KPT][kDecWaves] packed (> tau) << 16 | (== tau)
     const int NB = (T + block - 1) / block;
     const int nl = min(a.n_local, NB);
     const int NC = NB - nl;
     const int n = block_count(NB, block, a.budget_tokens, a.sparsity_bp, a.n_local, a.n_min);
     const int K = n - nl;  // candidates to pick (0 <= K <= NC)
-    const int base = KPT * tid;
     // slots that are not candidates hold the key 0, below every real key
     uint32_t key[KPT];
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) key[r] = (base + r < NC) ? float_key(sc[r]) : 0u;
+    for (int r = 0; r < KPT; ++r) key[r] = (tid + r * kDecThreads < NC) ? float_key(sc[r]) : 0u;
     // keys > tau are taken, and the first need_eq keys == tau (by index):
     // K = 0 takes nothing (no key exceeds 0xffffffff), K = NC every candidate
     uint32_t tau = (K == 0) ? 0xffffffffu : 0u;
@@ -179,8 +184,8 @@ __device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block
         uint32_t prefix = 0;  // of key - kmin, above the current digit
         int krem = K;         // keys still to take at or below the prefix
         int shift = (range == 0u) ? 0 : 32 - __clz(static_cast<int>(range));
-        // a wave whose first slot is past the candidates holds only keys 0
-        const bool live = wave * kWave * KPT < NC;  // wave-uniform
+        // a wave whose row-0 blocks are all past the candidates holds only keys 0
+        const bool live = wave * kWave < NC;  // wave-uniform
         // one radix pass over every key of the workgroup; returns the digit
         auto block_pass = [&]() __attribute__((always_inline)) {
             const int dbits = min(8, shift);
@@ -274,50 +279,58 @@ __device__ __forceinline__ int select_kept(const DecodeArgs& a, int T, int block
         tau = kmin + prefix;
         need_eq = krem;
     }
-    // positions in the ascending kept list: one packed scan of
-    // (keys > tau) << 16 | (keys == tau), the keys kept as bit masks
-    uint32_t gt_m = 0u, eq_m = 0u;
+    // Positions in the ascending kept list, which runs row by row (row r
+    // holds blocks r * kDecThreads .. + kDecThreads - 1) and, in a row, wave
+    // by wave and lane by lane.  Per (row, wave): the counts of keys > tau
+    // and == tau, packed, from ballots; every wave then forms the exclusive
+    // prefix of those counts in list order, and a key's place adds its
+    // lane's rank in the row's ballots.
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
-        gt_m |= (key[r] > tau) ? (1u << r) : 0u;
-        eq_m |= (key[r] == tau) ? (1u << r) : 0u;
+        const uint64_t mg = __ballot(key[r] > tau);
+        const uint64_t me = __ballot(key[r] == tau);
+        if (lane == 0) rowcnt[r * kDecWaves + wave] = (__popcll(mg) << 16) | __popcll(me);
     }
-    const int n_eq = __builtin_popcount(eq_m);
-    const int packed = (__builtin_popcount(gt_m) << 16) | n_eq;
-    const int incl = wave_incl_scan(packed);
-    if (lane == 63) red[2 * kDecWaves + wave] = incl;
     __syncthreads();
-    int before = 0;
+    // lane l holds entries l and l + 64 of the (row, wave) list (at most
+    // 16 x 8 = 128 entries); pre0/pre1: their exclusive prefixes
+    constexpr int NE = KPT * kDecWaves;
+    const int e0 = (lane < NE) ? rowcnt[lane] : 0;
+    const int e1 = (lane + 64 < NE) ? rowcnt[lane + 64] : 0;
+    const int inc0 = wave_incl_scan(e0);
+    const int tot0 = __builtin_amdgcn_readlane(inc0, 63);
+    const int pre0 = inc0 - e0;
+    const int pre1 = tot0 + wave_incl_scan(e1) - e1;
+    // the ballots below are formed again rather than kept from the counting
+    // loop (2 x KPT 64-bit masks would not fit in scalar registers)
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) before += (w < wave) ? red[2 * kDecWaves + w] : 0;
-    const int excl = before + incl - packed;
-    const int eq_rank = excl & 0xffff;  // this thread's keys == tau are ranked eq_rank, ...
-    int pos = (excl >> 16) + min(eq_rank, need_eq);
-    uint32_t take_m = gt_m;  // and those equal keys ranked below need_eq
-    for (int k = max(0, min(need_eq - eq_rank, n_eq)); k > 0; --k) {
-        take_m |= eq_m & (0u - eq_m);
-        eq_m &= eq_m - 1u;
-    }
-    // the taken keys, lowest index first; a key's page id is picked out of
-    // the registers with a select chain (no dynamic register indexing)
-    while (take_m != 0u) {
-        const int rr = __builtin_ctz(take_m);
-        int page = pg[0];
+    for (int r = 0; r < KPT; ++r) asm volatile("" : "+v"(key[r]));
 #pragma unroll
-        for (int i = 1; i < KPT; ++i) page = (rr == i) ? pg[i] : page;
-        kept[pos] = base + rr;
-        kept_page[pos] = page;
-        ++pos;
-        take_m &= take_m - 1u;
+    for (int r = 0; r < KPT; ++r) {
+        const int c = tid + r * kDecThreads;
+        const bool g = key[r] > tau, e = key[r] == tau;
+        const uint64_t mg = __ballot(g);
+        const uint64_t me = __ballot(e);
+        const int idx_e = r * kDecWaves + wave;  // wave-uniform
+        const int lsrc = __builtin_amdgcn_readfirstlane(idx_e & 63);
+        const int pre = (idx_e < 64) ? __builtin_amdgcn_readlane(pre0, lsrc)
+                                     : __builtin_amdgcn_readlane(pre1, lsrc);
+        if (g || e) {
+            const int below_g = (pre >> 16) + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                static_cast<uint32_t>(mg >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mg), 0u)));
+            const int below_e = (pre & 0xffff) + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                static_cast<uint32_t>(me >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(me), 0u)));
+            if (g || below_e < need_eq) {
+                const int pos = below_g + min(below_e, need_eq);
+                kept[pos] = c;
+                kept_page[pos] = pg[r];
+            }
+        }
     }
     // the local blocks follow the K picked candidates (their ids are the largest)
-#pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-        const int c = base + r;
-        if (c >= NC && c < NB) {
-            kept[K + c - NC] = c;
-            kept_page[K + c - NC] = pg[r];
-        }
+    if (tid < nl) {
+        kept[K + tid] = NC + tid;
+        kept_page[K + tid] = lpg;
     }
     __syncthreads();
     return n;
@@ -380,27 +393,16 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     int T_v = 0;
     float sc[NK];
     int pg[NK];
+    const int32_t* prow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
     if constexpr (SEL) {
         T_v = load_int_vgpr(c.seq_lens + s);
-        const int base = NK * threadIdx.x;
         const float* srow = a.scores + static_cast<int64_t>(grp) * a.score_stride;
-        if constexpr (NK >= 4) {
 #pragma unroll
-            for (int r = 0; r < NK; r += 4) {
-                const floatx4 v =
-                    *reinterpret_cast<const floatx4*>(srow + (base + r < a.score_stride ? base + r : 0));
-#pragma unroll
-                for (int k = 0; k < 4; ++k) sc[r + k] = v[k];
-            }
-        } else {
-            static_assert(NK == 2, "2, 4 or 8 blocks per thread");
-            const float2 v = *reinterpret_cast<const float2*>(srow + (base < a.score_stride ? base : 0));
-            sc[0] = v.x;
-            sc[1] = v.y;
+        for (int r = 0; r < NK; ++r) {
+            const int cb = threadIdx.x + r * kDecThreads;
+            sc[r] = srow[cb < a.score_stride ? cb : 0];
+            pg[r] = prow[cb < c.max_blocks ? cb : 0];
         }
-        const int32_t* prow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
-#pragma unroll
-        for (int r = 0; r < NK; ++r) pg[r] = prow[base + r < c.max_blocks ? base + r : 0];
     }
 
     // B operand of S^T = K Q^T: lane (g, col) holds q[head col][32ks + 8g .. +8]
@@ -425,9 +427,14 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     int cnt, T;
     if constexpr (SEL) {
         T = __builtin_amdgcn_readfirstlane(T_v);
+        // the local blocks' page ids (thread j: local block j), requested now
+        // and first needed at the end of the selection
+        const int NBs = (T + BLK - 1) / BLK;
+        const int nls = min(a.n_local, NBs);
+        const int lpg = (static_cast<int>(threadIdx.x) < nls) ? prow[NBs - nls + threadIdx.x] : 0;
         // the selection's scratch lies in the unit partials' LDS, written
         // only after it
-        cnt = select_kept<NK>(a, T, BLK, sc, pg, reinterpret_cast<int*>(smem), s_blk, s_page);
+        cnt = select_kept<NK>(a, T, BLK, sc, pg, lpg, reinterpret_cast<int*>(smem), s_blk, s_page);
         if (split == 0) {
             int32_t* orow = a.idx_out + static_cast<int64_t>(grp) * a.n_max;
             for (int i = threadIdx.x; i < a.n_max; i += kDecThreads)
@@ -438,7 +445,7 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
         __syncthreads();
     } else {
         const int32_t* idxrow = a.idx + static_cast<int64_t>(grp) * a.n_max;
-        const int32_t* ptrow = c.page_table + static_cast<int64_t>(s) * c.max_blocks;
+        const int32_t* ptrow = prow;
         const int nblk = (u1 > u0) ? (u1 - 1) / TPB - pb0 + 1 : 0;
         cnt = a.cnt[grp];
         T = c.seq_lens[s];
@@ -864,6 +871,8 @@ hipError_t launch_bf16(DecodeParams p, hipStream_t stream) {
     const bool gate = p.a.bias != nullptr;
     const bool sel = p.a.scores != nullptr;
     if (gate && sel) return hipErrorInvalidValue;
+    // SEL: candidate blocks of the longest possible row
+    const int cand = p.c.max_blocks - min(p.a.n_local, p.c.max_blocks);
     // SEL: the whole kept list (at most n_max entries) stays in LDS
     if (sel) p.max_blocks_per_wg = max(p.max_blocks_per_wg, p.a.n_max);
     // units: about one per wave, of 2 to BSA_DECODE_MAX_UNIT tiles (fewer,
@@ -895,14 +904,17 @@ hipError_t launch_bf16(DecodeParams p, hipStream_t stream) {
     else if (!sel)
         hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, 0>), grid, dim3(kDecThreads), shm,
                            stream, p);
-    else if (p.c.max_blocks <= 2 * kDecThreads)
+    else if (cand <= 2 * kDecThreads)
         hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, 2>), grid, dim3(kDecThreads), shm,
                            stream, p);
-    else if (p.c.max_blocks <= 4 * kDecThreads)
+    else if (cand <= 4 * kDecThreads)
         hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, 4>), grid, dim3(kDecThreads), shm,
                            stream, p);
-    else
+    else if (cand <= 8 * kDecThreads)
         hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, 8>), grid, dim3(kDecThreads), shm,
+                           stream, p);
+    else
+        hipLaunchKernelGGL((decode_bf16_kernel<D, BLK, false, 16>), grid, dim3(kDecThreads), shm,
                            stream, p);
     return hipGetLastError();
 }
@@ -943,6 +955,11 @@ int decode_splits(const CacheArgs& c, int n_max) {
     return S;
 }
 
+bool decode_selects(const CacheArgs& c, int n_local, int n_max) {
+    const int cand = c.max_blocks - min(n_local, c.max_blocks);
+    return c.dtype == kBF16 && cand <= kDecodeSelectSlots && n_max <= kDecodeSelectMaxKept;
+}
+
 hipError_t launch_combine_ragged(int dtype, int d, int rows, int splits, const float* o_part,
                                  const float* lse_part, void* o, float* lse,
                                  const int32_t* seq_lens, int rows_per_seq,
@@ -972,8 +989,7 @@ hipError_t launch_decode(const CacheArgs& c, const DecodeArgs& a, hipStream_t st
     const int tpb = c.block / 32;
     const int tiles = (a.n_max * tpb + a.splits - 1) / a.splits;
     DecodeParams p{c, a, tiles / tpb + 2, 0, 0};
-    if (a.scores && (c.dtype != kBF16 || c.max_blocks > kDecodeSelectSlots))
-        return hipErrorInvalidValue;
+    if (a.scores && !decode_selects(c, a.n_local, a.n_max)) return hipErrorInvalidValue;
     hipError_t err;
     if (c.dtype == kBF16)
         err = c.d == 64 ? launch_bf16_d<64>(p, stream) : launch_bf16_d<128>(p, stream);

@@ -294,12 +294,12 @@ BSA_API bsa_status bsa_sparse_decode(const bsa_layout* layout, const bsa_cache* 
  * Same references as those calls ("Rectified Sparse Attention ...",
  * Summary and Key points; "Simple Attention Sparsification", Method).
  * Results (the cache, idx, cnt, gate_bias, o, lse) are identical to those
- * calls made in that order with the same arguments.  For bf16 caches of at
- * most 4096 blocks per sequence (max_blocks <= 4096) without gate_bias, the
- * selection runs inside the decode launch: every decode workgroup selects
- * its group's kept blocks from the scores, which saves the top-n launch and
- * a dependent round trip; other cases make the four launches of the two
- * calls.
+ * calls made in that order with the same arguments.  For bf16 caches whose
+ * rows hold at most 8192 candidate blocks (max_blocks - n_local <= 8192),
+ * with n_max <= 4096 and no gate_bias, the selection runs inside the decode
+ * launch: every decode workgroup selects its group's kept blocks from the
+ * scores, which saves the top-n launch and a dependent round trip; other
+ * cases make the four launches of the two calls.
  * k_new, v_new: [B][Hkv][1][d]; q: [B][Hq][d] (KV dtype; the caller has
  *   already advanced seq_lens by one).  idx, cnt: OUT, as bsa_select_blocks
  *   writes them (row length params->n_max).  o, lse: OUT, as

@@ -2,12 +2,12 @@
 shape it gives the cache, descriptors, idx, cnt, o and lse of
 bsa_append_select followed by bsa_sparse_decode (bit for bit: the decode's
 split ranges and units are the same), step after step, and the oracle's
-selection, o and lse.  Rows of at most 4096 blocks (bf16, no log-gate bias)
-select inside the decode launch: those cases cover two, four and eight
-blocks per thread up to the last thread, rows shorter than the capacity,
-single-block sequences, a budget covering the whole context, long runs of
-tied scores and both descriptor kinds; the others check the four-launch
-form."""
+selection, o and lse.  Rows of at most 8192 candidate blocks (bf16, no
+log-gate bias) select inside the decode launch: those cases cover two, four,
+eight and sixteen rows per thread up to the last thread's last row, rows
+shorter than the capacity, single-block sequences, a budget covering the
+whole context, long runs of tied scores and both descriptor kinds; the
+others check the four-launch form."""
 import math
 
 import numpy as np
@@ -41,10 +41,14 @@ STEP_CASES = [
     # thread (3126 blocks of capacity, the short rows in one or two waves)
     (BF16, 64, 32, MINMAX, 4, 1, [40000], 0, 9000, 2, 4, 2, False),
     (BF16, 128, 32, MINMAX, 8, 2, [100000, 16384, 3000, 40000], 0, 9000, 2, 16, 2, False),
-    # 4096 blocks of capacity: thread 511 holds blocks 4088 .. 4095
+    # 4096 blocks of capacity (eight rows per thread)
     (BF16, 64, 32, MEAN, 4, 1, [131069], 0, 9500, 2, 0, 3, False),
-    # the four-launch form: more than 4096 blocks, a log-gate bias, fp32
+    # sixteen rows per thread: 4374 candidates, and 8192 (the last thread's
+    # last row is a candidate; the two local blocks lie past the rows)
     (BF16, 64, 32, MINMAX, 4, 1, [140000], 0, 9000, 2, 4, 2, False),
+    (BF16, 64, 32, MINMAX, 4, 1, [262176], 0, 9000, 2, 16, 3, False),
+    # the four-launch form: more than 8192 candidates, a log-gate bias, fp32
+    (BF16, 64, 32, MINMAX, 4, 1, [300000], 0, 9500, 2, 4, 2, False),
     (BF16, 128, 64, MINMAX, 8, 2, [3000, 1700], 0, 9000, 2, 4, 2, True),
     (F32, 64, 64, MINMAX, 4, 1, [2049], 512, 0, 1, 2, 2, False),
 ]
