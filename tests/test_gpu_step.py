@@ -34,6 +34,9 @@ STEP_CASES = [
     (BF16, 128, 64, MINMAX, 8, 2, [1, 64, 65, 2000], 0, 8000, 1, 3, 2, False),
     # budget >= context: every candidate kept
     (BF16, 64, 64, MINMAX, 4, 2, [700, 1283], 64 * 40, 0, 1, 0, 2, False),
+    # three local blocks against sequences of 1-2 blocks (every block local,
+    # no candidate) beside a longer one
+    (BF16, 128, 64, MINMAX, 8, 2, [1, 100, 1500], 0, 9000, 3, 6, 2, False),
     # G = 1 and G = 16 groups
     (BF16, 64, 64, MINMAX, 2, 2, [1900], 0, 9000, 3, 0, 2, False),
     (BF16, 128, 64, MINMAX, 16, 1, [4000], 0, 9500, 2, 2, 2, False),
@@ -171,3 +174,50 @@ def test_step_long_run_of_ties():
         ref = oracle_decode(P, q, [K[:, :now]], [V[:, :now]], [now], L)
         compare_step(L, one[0], one[1], one[2], one[3], ref)
         assert {3, 200, 555, 998} <= set(ref[(0, 0)][0].tolist())
+
+
+def test_step_checked_build_matches_default():
+    """The checked build (host-side contract checks, then the same kernels)
+    gives the default build's results for the one-call step, bit for bit, on
+    the in-launch form and on the four-launch form (log-gate bias)."""
+    import torch
+    d, blk, Hq, Hkv = 128, 64, 8, 2
+    lengths = [3000, 1700]
+    L = bsa.Layout(2, Hq, Hkv, d, blk, 60, BF16, MINMAX)
+    q, Ks, Vs, _ = make_inputs(61, 2, Hq, Hkv, d, [T + 2 for T in lengths], BF16, MINMAX)
+    q_dev = to_dev(q, L)
+    outs = []
+    for path in (bsa.LIB_DEFAULT, bsa.LIB_CHECKED):
+        before = bsa.use_library(path)
+        try:
+            c = bsa.allocate_cache(L, page_table=random_page_table(L, 12))
+            for t in (c.k_pool, c.v_pool, c.desc):
+                t.zero_()
+            prefill(L, c, Ks, Vs, lengths)
+            res = []
+            for gated in (False, True):
+                P = bsa.SelectParams(sparsity_bp=9000, n_local=2, n_min=4)
+                P.n_max = bsa.block_count(P, L.max_blocks, blk)
+                ws = torch.empty(bsa.workspace_size(L, bsa.OP_STEP, P.n_max), dtype=torch.uint8,
+                                 device="cuda")
+                idx = torch.full((2, Hkv, P.n_max), -7, dtype=torch.int32, device="cuda")
+                cnt = torch.full((2, Hkv), -7, dtype=torch.int32, device="cuda")
+                o = torch.full((2, Hq, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+                lse = torch.full((2, Hq), float("nan"), dtype=torch.float32, device="cuda")
+                if gated:
+                    P.gate_tau = 0.05
+                    P.gate_bias = torch.zeros(2, Hkv, P.n_max, dtype=torch.float32, device="cuda")
+                step = 1 if gated else 0
+                kn = to_dev(np.stack([Ks[s][:, lengths[s] + step] for s in range(2)])[:, :, None], L)
+                vn = to_dev(np.stack([Vs[s][:, lengths[s] + step] for s in range(2)])[:, :, None], L)
+                c.seq_lens += 1
+                bsa.append_select_decode(L, c, kn, vn, q_dev, P, idx, cnt, 1 / math.sqrt(d), o,
+                                         lse, ws)
+                torch.cuda.synchronize()
+                res += [idx, cnt, o, lse] + ([P.gate_bias] if gated else [])
+            res += [c.k_pool, c.v_pool, c.desc]
+            outs.append(res)
+        finally:
+            bsa.use_library(before)
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
