@@ -387,9 +387,9 @@ __attribute__((amdgpu_waves_per_eu(BSA_DECODE_WAVES_PER_EU, 8))) void decode_bf1
     const int g = lane >> 4;
     const int col = lane & 15;
 
-    // SEL: the length, this thread's NK scores and their blocks' page ids,
-    // requested before the queries (loads past the row read its first
-    // entries; the row stride is a multiple of 4)
+    // SEL: the length, this thread's NK scores and their blocks' page ids
+    // (one coalesced wave load per row), requested before the queries; slots
+    // past the row read its first entry
     int T_v = 0;
     float sc[NK];
     int pg[NK];
