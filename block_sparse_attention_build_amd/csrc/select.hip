@@ -875,15 +875,7 @@ hipError_t launch_append_score_only(const CacheArgs& c, const void* k_new, const
 
 hipError_t launch_append_select(const CacheArgs& c, const void* k_new, const void* v_new,
                                 const SelectArgs& s, hipStream_t stream) {
-    ScoreParams sp{c, s, score_stride(c.max_blocks)};
-    KvWriteParams kp{c, kModeAppend, k_new, v_new, 1, nullptr};
-    hipError_t err;
-    if (c.dtype == kBF16)
-        err = c.desc_kind == kMinMax ? launch_append_score_d<kBF16, kMinMax>(sp, kp, stream)
-                                     : launch_append_score_d<kBF16, kMeanPool>(sp, kp, stream);
-    else
-        err = c.desc_kind == kMinMax ? launch_append_score_d<kF32, kMinMax>(sp, kp, stream)
-                                     : launch_append_score_d<kF32, kMeanPool>(sp, kp, stream);
+    const hipError_t err = launch_append_score_only(c, k_new, v_new, s, stream);
     if (err != hipSuccess) return err;
     return launch_topn(c, s, stream);
 }
