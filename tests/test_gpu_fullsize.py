@@ -113,13 +113,16 @@ class Filled:
             del K, V
         torch.cuda.synchronize()
 
+    def next_tokens(self):
+        """Token T_s of every sequence, [B, Hkv, 1, d] K and V on the device."""
+        torch = _torch()
+        toks = [self.device_tokens(s, T, T + 1) for s, T in enumerate(self.T)]
+        return torch.cat([k for k, _ in toks]), torch.cat([v for _, v in toks])
+
     def append_one(self):
         """Append token T_s of every sequence (one decode step's append)."""
         torch = _torch()
-        w = self.w
-        toks = [self.device_tokens(s, T, T + 1) for s, T in enumerate(self.T)]
-        kn = torch.cat([k for k, _ in toks])
-        vn = torch.cat([v for _, v in toks])
+        kn, vn = self.next_tokens()
         self.cache.seq_lens += 1
         bsa.build_block_desc(self.L, self.cache, kn, vn, 1)
         self.T = [T + 1 for T in self.T]
@@ -127,7 +130,7 @@ class Filled:
 
     def workspace(self, f=0):
         torch = _torch()
-        n = max([bsa.workspace_size(self.L, bsa.OP_SELECT, P.n_max) for P in self.params.values()]
+        n = max([bsa.workspace_size(self.L, bsa.OP_STEP, P.n_max) for P in self.params.values()]
                 + [bsa.workspace_size(self.L, bsa.OP_DECODE, P.n_max) for P in self.params.values()]
                 + ([bsa.workspace_size(self.L, bsa.OP_RECTIFY, f)] if f else []))
         return torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -227,7 +230,12 @@ def check_every_group(F, P, idx, cnt, o, lse, scale):
           f"worst score inversion {worst:.2e} of the term magnitude", flush=True)
 
 
-def select_decode_and_check(F, P, ws, every_group=False):
+def select_decode_and_check(F, P, ws, every_group=False, one_call=False):
+    """Select and decode at the current lengths (one_call=False: the cache
+    already holds the step's token; bsa_select_blocks + bsa_sparse_decode),
+    or append token T_s of every sequence and do the whole step in one
+    bsa_append_select_decode call, the call the benchmark times
+    (one_call=True); then check against the oracle."""
     torch = _torch()
     w, L = F.w, F.L
     G = w.G
@@ -238,8 +246,14 @@ def select_decode_and_check(F, P, ws, every_group=False):
     o = torch.full((w.B, w.Hq, w.d), float("nan"), dtype=tdt, device="cuda")
     lse = torch.full((w.B, w.Hq), float("nan"), dtype=torch.float32, device="cuda")
     scale = 1.0 / math.sqrt(w.d)
-    bsa.select_blocks(L, F.cache, q_dev, P, idx, cnt, ws)
-    bsa.sparse_decode(L, F.cache, q_dev, idx, cnt, P.n_max, scale, o, lse, ws)
+    if one_call:
+        kn, vn = F.next_tokens()
+        F.cache.seq_lens += 1
+        F.T = [T + 1 for T in F.T]
+        bsa.append_select_decode(L, F.cache, kn, vn, q_dev, P, idx, cnt, scale, o, lse, ws)
+    else:
+        bsa.select_blocks(L, F.cache, q_dev, P, idx, cnt, ws)
+        bsa.sparse_decode(L, F.cache, q_dev, idx, cnt, P.n_max, scale, o, lse, ws)
     torch.cuda.synchronize()
     idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
     o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
@@ -262,11 +276,12 @@ def select_decode_and_check(F, P, ws, every_group=False):
         check_every_group(F, P, idx, cnt, o, lse, scale)
 
 
+@pytest.mark.parametrize("form", ["one_call", "separate"])
 @pytest.mark.parametrize("name,sampled", [
     ("qwen3_4b_32k", [(0, h) for h in range(8)]),
     ("batched_64k_gate", [(0, 0), (3, 5), (7, 7)]),
 ])
-def test_fullsize_decode_step(name, sampled):
+def test_fullsize_decode_step(name, sampled, form):
     torch = _torch()
     w = W.get(name)
     gate = None
@@ -279,8 +294,11 @@ def test_fullsize_decode_step(name, sampled):
     P = F.params[w.sparsity_bp]
     F.enforce([P], [T + 1 for T in F.T])
     F.allocate_and_prefill()
-    F.append_one()
-    select_decode_and_check(F, P, F.workspace(), every_group=True)
+    if form == "one_call":  # in-launch selection (rows of 575 and 542 candidates)
+        select_decode_and_check(F, P, F.workspace(), every_group=True, one_call=True)
+    else:
+        F.append_one()
+        select_decode_and_check(F, P, F.workspace(), every_group=True)
 
 
 def test_split_cap_decides_the_split_count():
@@ -380,8 +398,9 @@ def test_fullsize_resa_rectify_then_decode(f):
 
 def test_fullsize_resa_loop_two_rectifies():
     """The ragged ReSA loop at full size for 2f steps: every step appends a
-    token and selects (the fused append + select the benchmark times) and
-    decodes; after steps f and 2f the last f tokens are rectified.  On two
+    token, selects and decodes in one bsa_append_select_decode call (the
+    call the benchmark times; 2110 candidates select in-launch); after steps
+    f and 2f the last f tokens are rectified.  On two
     sampled groups (the 16K and the 128K sequence) the oracle follows on host
     copies that take the same rewrites: the rectify rows at each rectify, and
     the selection (bit-exact), o and lse at sampled steps before, between and
@@ -421,8 +440,8 @@ def test_fullsize_resa_loop_two_rectifies():
         F.cache.seq_lens += 1
         F.T = [T + 1 for T in F.T]
         q_dev = torch.from_numpy(qh).to("cuda", tdt)
-        bsa.append_select(F.L, F.cache, kn, vn, q_dev, P, idx, cnt, ws)
-        bsa.sparse_decode(F.L, F.cache, q_dev, idx, cnt, P.n_max, scale, o, lse, ws)
+        # the step as the benchmark times it: one call, selecting in-launch
+        bsa.append_select_decode(F.L, F.cache, kn, vn, q_dev, P, idx, cnt, scale, o, lse, ws)
         if k in check_at:
             torch.cuda.synchronize()
             gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
