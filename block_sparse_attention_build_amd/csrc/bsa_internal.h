@@ -63,10 +63,10 @@ struct DecodeArgs {
     float* lse_part;   // [B*Hq][S]  (base-2 log-sum-exp of the scaled logits)
     void* o;
     float* lse;
-    // In-workgroup selection (bf16, max_blocks <= kDecodeSelectSlots, no
-    // bias): with scores set, every decode workgroup selects its group's
-    // kept blocks from the score row itself, idx/cnt above are ignored, and
-    // the first split of each group writes the kept list to idx_out/cnt_out.
+    // In-workgroup selection (bf16, no bias, decode_selects() true): with
+    // scores set, every decode workgroup selects its group's kept blocks
+    // from the score row itself, idx/cnt above are ignored, and the first
+    // split of each group writes the kept list to idx_out/cnt_out.
     const float* scores = nullptr;  // [B*Hkv][score_stride]
     int score_stride = 0;
     int budget_tokens = 0, sparsity_bp = 0, n_local = 1, n_min = 0;
