@@ -49,7 +49,8 @@
  *     every call:   0 <= seq_lens[s] <= max_blocks*block, and every block
  *                   holding tokens has a page id >= 0 (the pool size is the
  *                   caller's, so the upper bound is not checked);
- *     append:       seq_lens[s] >= n_new (bsa_append_select: >= 1);
+ *     append:       seq_lens[s] >= n_new (bsa_append_select and
+ *                   bsa_append_select_decode: >= 1);
  *     decode:       0 <= cnt <= n_max, the first cnt ids of each idx row are
  *                   distinct and below ceil(seq_lens[s] / block), and their
  *                   gate biases (gated call) are finite;
