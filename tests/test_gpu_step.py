@@ -7,7 +7,8 @@ log-gate bias) select inside the decode launch: those cases cover two, four,
 eight and sixteen rows per thread up to the last thread's last row, rows
 shorter than the capacity, single-block sequences, a budget covering the
 whole context, long runs of tied scores and both descriptor kinds; the
-others check the four-launch form."""
+others check the four-launch form.  Seeded random shapes add combinations no
+hand-written case names."""
 import math
 
 import numpy as np
@@ -91,6 +92,46 @@ def _step_pair(L, P, caches, q_dev, kn, vn, scale, ws, gated):
 
 @pytest.mark.parametrize("case", STEP_CASES, ids=[f"s{i}" for i in range(len(STEP_CASES))])
 def test_step_equals_the_calls_and_the_oracle(case):
+    _run_step_case(case, 41)
+
+
+def _draw(seed):
+    """A seeded random step case: mostly short rows of any block size, a
+    quarter long rows at b = 32 (up to about 4700 blocks, every in-launch
+    tier), some fp32 and some with the log-gate bias (the four-launch form)."""
+    rng = np.random.Generator(np.random.PCG64(7700 + seed))
+    gated = rng.random() < 0.2
+    dtype = F32 if rng.random() < 0.15 else BF16
+    kind = MINMAX if rng.random() < 0.7 else MEAN
+    if rng.random() < 0.25:
+        d, blk, Hkv = 64, 32, 1
+        G = int(rng.choice([1, 2, 4]))
+        B = int(rng.integers(1, 3))
+        lengths = [int(x) for x in rng.integers(1, 150000, size=B)]
+    else:
+        d = int(rng.choice([64, 128]))
+        blk = int(rng.choice([32, 64, 128, 256]))
+        Hkv = int(rng.integers(1, 5))
+        G = int(rng.choice([1, 2, 3, 4, 5, 8]))
+        B = int(rng.integers(1, 5))
+        lengths = [int(x) for x in rng.integers(1, 40 * blk, size=B)]
+    if rng.random() < 0.4:
+        budget, bp = int(rng.integers(1, 24)) * blk, 0
+    else:
+        budget, bp = 0, int(rng.choice([5000, 8000, 9000, 9500]))
+    n_local = int(rng.integers(1, 4))
+    n_min = int(rng.integers(0, 6))
+    return (dtype, d, blk, kind, G * Hkv, Hkv, lengths, budget, bp, n_local, n_min, 2, gated)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shape_step(seed):
+    case = _draw(seed)
+    print(f"seed {seed}: {case}", flush=True)
+    _run_step_case(case, 800 + seed)
+
+
+def _run_step_case(case, seed):
     import torch
     dtype, d, blk, kind, Hq, Hkv, lengths, budget, bp, nl, nm, steps, gated = case
     B = len(lengths)
@@ -99,7 +140,7 @@ def test_step_equals_the_calls_and_the_oracle(case):
     P = bsa.SelectParams(budget_tokens=budget, sparsity_bp=bp, n_local=nl, n_min=nm)
     P.n_max = bsa.block_count(P, max_blocks, blk)
     total = [T + steps for T in lengths]
-    q, Ks, Vs, Wg = make_inputs(41 + B, B, Hq, Hkv, d, total, dtype, kind)
+    q, Ks, Vs, Wg = make_inputs(seed + B, B, Hq, Hkv, d, total, dtype, kind)
     if not gated:
         enforce_gap(L, P, q, Ks, [[T + i + 1 for i in range(steps)] for T in lengths], W_gate=Wg)
     if Wg is not None:
